@@ -1,0 +1,130 @@
+"""Pure-Python, loop-only twin of the block oracle, for tiny inputs.
+
+TEST INFRASTRUCTURE.  Only ``tests/`` may import this module.
+
+It is written independently of ``dit_block`` so that the two pin each other:
+every product is an explicit loop, the rotary step multiplies complex numbers
+``(x_2p + i x_2p+1) * e^(i angle)`` instead of applying a 2x2 rotation, the
+rotary angles come from grid positions here rather than from ``rope_tables``,
+and softmax is an explicit max / exp / sum over each query's keys.  The
+computation is the block the MOSS-Image transformer page (TensorFold PR #1528,
+"What it adds") describes, under the readings stated in ``dit_block``.
+"""
+from __future__ import annotations
+
+import cmath
+import math
+from operator import mul
+
+
+def _dot(a, b) -> float:
+    return math.fsum(map(mul, a, b))
+
+
+def _matvec_rows(rows, w):
+    """rows [n][k] times w[o][k]^T -> [n][o]."""
+    return [[_dot(r, wo) for wo in w] for r in rows]
+
+
+def _silu(z: float) -> float:
+    if z < -700.0:
+        return 0.0
+    return z / (1.0 + math.exp(-z))
+
+
+def _rms(row, eps: float):
+    ms = math.fsum(v * v for v in row) / len(row)
+    inv = 1.0 / math.sqrt(ms + eps)
+    return [v * inv for v in row]
+
+
+def positions(n_txt: int, grid_h: int, grid_w: int):
+    """(y, x) grid position per row; text rows sit at (0, 0)."""
+    pos = [(0, 0)] * n_txt
+    for y in range(grid_h):
+        for x in range(grid_w):
+            pos.append((y, x))
+    return pos
+
+
+def angles(pos, theta: float, head_dim: int):
+    """Rotary angle per (row, pair): y-axis frequencies on the first half of pairs."""
+    half = head_dim // 4
+    out = []
+    for (y, x) in pos:
+        row = []
+        for p in range(head_dim // 2):
+            if p < half:
+                row.append(y * theta ** (-p / half))
+            else:
+                row.append(x * theta ** (-(p - half) / half))
+        out.append(row)
+    return out
+
+
+def _rotate(vec, ang_row):
+    out = []
+    for p, a in enumerate(ang_row):
+        z = complex(vec[2 * p], vec[2 * p + 1]) * cmath.exp(1j * a)
+        out.extend((z.real, z.imag))
+    return out
+
+
+def block(x, txt, txt_len, cond, w, ang, eps: float):
+    """One block for nested-list inputs.
+
+    x [B][n_img][D], txt [B][n_txt][D], txt_len [B], cond [B][D]; w holds
+    nested lists ``w_mod [6D][D]``, ``w_qkv [3D][D]``, ``q_gain [128]``,
+    ``k_gain [128]``, ``w_out [D][D]``, ``w_up [2F][D]``, ``w_down [D][F]``;
+    ang [T][64] rotary angles.  Returns the block output [B][T][D].
+    """
+    hd = len(w["q_gain"])
+    out = []
+    for b in range(len(x)):
+        n_txt = len(txt[b])
+        rows = [list(r) if i < txt_len[b] else [0.0] * len(r) for i, r in enumerate(txt[b])]
+        rows += [list(r) for r in x[b]]
+        out.append(block_rows(rows, txt_len[b], n_txt, cond[b], w, ang, eps, hd))
+    return out
+
+
+def block_rows(h0, n_valid_txt: int, n_txt: int, cond_b, w, ang, eps: float, hd: int):
+    d = len(h0[0])
+    t = len(h0)
+    nh = d // hd
+    f = len(w["w_down"][0])
+    s = [_silu(c) for c in cond_b]
+    mod = [_dot(wr, s) for wr in w["w_mod"]]
+    shift1, scale1, gate1 = mod[0:d], mod[d:2 * d], mod[2 * d:3 * d]
+    shift2, scale2, gate2 = mod[3 * d:4 * d], mod[4 * d:5 * d], mod[5 * d:6 * d]
+
+    a = [[n * (1.0 + sc) + sh for n, sc, sh in zip(_rms(r, eps), scale1, shift1)] for r in h0]
+    qkv = _matvec_rows(a, w["w_qkv"])
+    key_ok = [not (n_valid_txt <= j < n_txt) for j in range(t)]
+    o = [[0.0] * d for _ in range(t)]
+    inv_sqrt = 1.0 / math.sqrt(hd)
+    for e in range(nh):
+        qs, ks, vs = [], [], []
+        for r in range(t):
+            q = qkv[r][e * hd:(e + 1) * hd]
+            k = qkv[r][d + e * hd:d + (e + 1) * hd]
+            v = qkv[r][2 * d + e * hd:2 * d + (e + 1) * hd]
+            q = [g * val for g, val in zip(w["q_gain"], _rms(q, eps))]
+            k = [g * val for g, val in zip(w["k_gain"], _rms(k, eps))]
+            qs.append(_rotate(q, ang[r]))
+            ks.append(_rotate(k, ang[r]))
+            vs.append(v)
+        for i in range(t):
+            scores = [(_dot(qs[i], ks[j]) * inv_sqrt if key_ok[j] else None) for j in range(t)]
+            mx = max(sv for sv in scores if sv is not None)
+            ps = [(math.exp(sv - mx) if sv is not None else 0.0) for sv in scores]
+            tot = math.fsum(ps)
+            for c in range(hd):
+                o[i][e * hd + c] = math.fsum(ps[j] * vs[j][c] for j in range(t)) / tot
+    o2 = _matvec_rows(o, w["w_out"])
+    h1 = [[hv + g * ov for hv, g, ov in zip(hr, gate1, orow)] for hr, orow in zip(h0, o2)]
+    m = [[n * (1.0 + sc) + sh for n, sc, sh in zip(_rms(r, eps), scale2, shift2)] for r in h1]
+    u = _matvec_rows(m, w["w_up"])
+    z = [[_silu(ur[c]) * ur[f + c] for c in range(f)] for ur in u]
+    y = _matvec_rows(z, w["w_down"])
+    return [[hv + g * yv for hv, g, yv in zip(hr, gate2, yr)] for hr, yr in zip(h1, y)]

@@ -1,0 +1,158 @@
+"""Planted mistakes in the oracle must turn at least one pin red (CPU only).
+
+Each mutant replaces one oracle function with a plausible wrong version (a
+dropped term, a wrong sign, index or axis, swapped operands), in the manner of
+the pages' planted controls that "drop or add one rounding point" and must
+come out red (MOSS-Image encoder page, PR #1512, "Receipt").  The mistakes are
+planted in the oracle, on the CPU; nothing here touches the GPU library.
+"""
+import numpy as np
+import pytest
+
+from oracle import dit_block as ob
+
+from . import oracle_pins as P
+
+_orig = {name: getattr(ob, name) for name in (
+    "silu", "rms_normalize", "adaln_modulation", "split_modulation", "modulated_rmsnorm", "rope_tables",
+    "rope_rotate", "qk_norm_rope", "attention", "silu_gate", "gated_add", "join_rows", "key_mask")}
+
+
+def _silu_sign(z):
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(z))
+
+
+def _rms_eps_outside(h, eps):
+    h = np.asarray(h, dtype=np.float64)
+    return h / (np.sqrt(np.mean(h * h, axis=-1, keepdims=True)) + eps)
+
+
+def _rms_sum(h, eps):
+    h = np.asarray(h, dtype=np.float64)
+    return h / np.sqrt(np.sum(h * h, axis=-1, keepdims=True) + eps)
+
+
+def _mod_no_silu(cond, w_mod):
+    return np.asarray(cond) @ np.asarray(w_mod).T
+
+
+def _split_swapped(mod, d):
+    r = _orig["split_modulation"](mod, d)
+    r["shift1"], r["scale1"] = r["scale1"], r["shift1"]
+    return r
+
+
+def _split_gates_swapped(mod, d):
+    r = _orig["split_modulation"](mod, d)
+    r["gate1"], r["gate2"] = r["gate2"], r["gate1"]
+    return r
+
+
+def _modnorm_no_one(h, shift, scale, eps):
+    return ob.rms_normalize(h, eps) * scale + shift
+
+
+def _rope_axes_swapped(n_txt, gh, gw, theta=10000.0, head_dim=128):
+    cos, sin = _orig["rope_tables"](n_txt, gh, gw, theta, head_dim)
+    h = head_dim // 4
+    return (np.concatenate([cos[:, h:], cos[:, :h]], axis=1), np.concatenate([sin[:, h:], sin[:, :h]], axis=1))
+
+
+def _rope_freq_wrong(n_txt, gh, gw, theta=10000.0, head_dim=128):
+    return _orig["rope_tables"](n_txt, gh, gw, theta ** 2, head_dim)
+
+
+def _rotate_sign(x, cos, sin):
+    return _orig["rope_rotate"](x, cos, -sin)
+
+
+def _rotate_half(x, cos, sin):
+    x = np.asarray(x, dtype=np.float64)
+    p = x.shape[-1] // 2
+    x1, x2 = x[..., :p], x[..., p:]
+    return np.concatenate([x1 * cos - x2 * sin, x1 * sin + x2 * cos], axis=-1)
+
+
+def _qk_gains_swapped(q, k, qg, kg, cos, sin, eps, rnd=lambda a: a):
+    return _orig["qk_norm_rope"](q, k, kg, qg, cos, sin, eps, rnd)
+
+
+def _qk_no_norm(q, k, qg, kg, cos, sin, eps, rnd=lambda a: a):
+    return rnd(ob.rope_rotate(q * qg, cos, sin)), rnd(ob.rope_rotate(k * kg, cos, sin))
+
+
+def _attn_no_scale(q, k, v, valid, rnd=lambda a: a):
+    return _orig["attention"](q * np.sqrt(q.shape[-1]), k, v, valid, rnd)
+
+
+def _attn_no_mask(q, k, v, valid, rnd=lambda a: a):
+    return _orig["attention"](q, k, v, np.ones_like(valid), rnd)
+
+
+def _attn_query_axis(q, k, v, valid, rnd=lambda a: a):
+    s = (q @ np.swapaxes(k, -1, -2)) / np.sqrt(q.shape[-1])
+    s = np.where(np.asarray(valid, dtype=bool)[None, None, :], s, -np.inf)
+    p = np.exp(s - np.max(s, axis=-2, keepdims=True))
+    p = np.nan_to_num(p / np.sum(p, axis=-2, keepdims=True))
+    return p @ v
+
+
+def _attn_k_for_v(q, k, v, valid, rnd=lambda a: a):
+    return _orig["attention"](q, k, k, valid, rnd)
+
+
+def _silu_gate_halves(u, f):
+    return ob.silu(u[..., f:]) * u[..., :f]
+
+
+def _gated_add_no_gate(h, gate, y):
+    return h + y
+
+
+def _join_pad_kept(x, txt, txt_len):
+    return np.concatenate([np.asarray(txt, dtype=np.float64), np.asarray(x, dtype=np.float64)], axis=1)
+
+
+def _key_mask_off_by_one(n_txt, n_img, txt_len):
+    m = np.ones((len(txt_len), n_txt + n_img), dtype=bool)
+    for b, n in enumerate(txt_len):
+        m[b, int(n) + 1:n_txt] = False
+    return m
+
+
+MUTANTS = {
+    "silu_sign": ("silu", _silu_sign),
+    "rms_eps_outside_sqrt": ("rms_normalize", _rms_eps_outside),
+    "rms_sum_not_mean": ("rms_normalize", _rms_sum),
+    "modulation_without_silu": ("adaln_modulation", _mod_no_silu),
+    "modulation_shift_scale_swapped": ("split_modulation", _split_swapped),
+    "modulation_gates_swapped": ("split_modulation", _split_gates_swapped),
+    "modnorm_scale_not_one_plus": ("modulated_rmsnorm", _modnorm_no_one),
+    "rope_axes_swapped": ("rope_tables", _rope_axes_swapped),
+    "rope_frequency_base": ("rope_tables", _rope_freq_wrong),
+    "rope_sin_sign": ("rope_rotate", _rotate_sign),
+    "rope_half_split_pairs": ("rope_rotate", _rotate_half),
+    "qk_gains_swapped": ("qk_norm_rope", _qk_gains_swapped),
+    "qk_norm_dropped": ("qk_norm_rope", _qk_no_norm),
+    "attention_scale_dropped": ("attention", _attn_no_scale),
+    "attention_mask_dropped": ("attention", _attn_no_mask),
+    "softmax_over_queries": ("attention", _attn_query_axis),
+    "attention_k_as_v": ("attention", _attn_k_for_v),
+    "silu_gate_halves_swapped": ("silu_gate", _silu_gate_halves),
+    "gated_add_gate_dropped": ("gated_add", _gated_add_no_gate),
+    "pad_rows_not_zeroed": ("join_rows", _join_pad_kept),
+    "key_mask_off_by_one": ("key_mask", _key_mask_off_by_one),
+}
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert P.failing_pins() == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(ob, attr, fn)
+    assert P.failing_pins(), f"planted mistake {name!r} passed every pin"

@@ -1,0 +1,42 @@
+"""The oracle against its pins (CPU only)."""
+import numpy as np
+import pytest
+
+from diffusion_transformer_denoiser_amd import synth
+from oracle import dit_block as ob
+
+from . import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin()
+
+
+def test_brute_force_c0():
+    """The NumPy oracle equals the loop-only brute force on the small workload (72 rows, D=256)."""
+    geom = synth.CONFIGS["c0"]
+    x, txt, lens, cond, ws = P.f64_inputs(geom, seed=0)
+    cos, sin = ob.rope_tables(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, geom.head_dim)
+    got = ob.block_forward(x, txt, lens, cond, ws[0], cos, sin, geom.eps)
+    ref = P._brute_block(geom, x, txt, lens, cond, ws[0])
+    P._close(got, ref, 1e-12)
+
+
+def test_rounded_mode_close_to_exact():
+    """The bf16-rounding-point mode stays near the exact mode, step by step.
+
+    At the small workload the block's update is about 1% of the residual, so
+    the output is compared at bf16 resolution and every intermediate by
+    cosine.
+    """
+    geom = synth.CONFIGS["c0"]
+    x, txt, lens, cond, ws = P.f64_inputs(geom, seed=0)
+    cos, sin = ob.rope_tables(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, geom.head_dim)
+    a, sa = ob.block_forward(x, txt, lens, cond, ws[0], cos, sin, geom.eps, keep=True)
+    b, sb = ob.block_forward(x, txt, lens, cond, ws[0], cos, sin, geom.eps, rounded=True, keep=True)
+    for k in sa:
+        u, v = sa[k].ravel(), sb[k].ravel()
+        assert 1.0 - float(u @ v / np.linalg.norm(u) / np.linalg.norm(v)) < 5e-5, k
+    assert np.max(np.abs(a - b)) <= 2.0 ** -7 * np.max(np.abs(a))
+    assert not np.array_equal(a, b)
