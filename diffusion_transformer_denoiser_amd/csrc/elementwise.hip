@@ -1,0 +1,249 @@
+// Bandwidth-bound kernels of the block: row join, adaLN GEMV, modulated
+// RMSNorm, gated residual add, SiLU-gated product, rotary tables.
+//
+// The MOSS-Image transformer page (TensorFold PR #1528, "What it adds") names
+// the modulated RMSNorm, SiLU and gated-add kernels and the precision policy
+// (bf16 storage, fp32 sums and norms).  Every kernel here moves 16 bytes per
+// lane per access (eight bf16) so that a wavefront touches 1 KiB contiguous.
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---- a0: h0 = [txt; x], pad text rows read as zero -------------------------
+__global__ __launch_bounds__(kThreads) void join_rows_kernel(const u32x4* __restrict__ x,
+                                                             const u32x4* __restrict__ txt, ItemLens lens,
+                                                             u32x4* __restrict__ out, int n_txt, int n_img,
+                                                             int chunks_per_row, long total) {
+  const int rows = n_txt + n_img;
+  for (long i = (long)blockIdx.x * kThreads + threadIdx.x; i < total; i += (long)gridDim.x * kThreads) {
+    const long row = i / chunks_per_row;
+    const int c = (int)(i - row * chunks_per_row);
+    const int b = (int)(row / rows);
+    const int r = (int)(row - (long)b * rows);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < n_txt) {
+      if (r < lens.len[b]) v = txt[((long)b * n_txt + r) * chunks_per_row + c];
+    } else {
+      v = x[((long)b * n_img + (r - n_txt)) * chunks_per_row + c];
+    }
+    out[i] = v;
+  }
+}
+
+// ---- a1: s = SiLU(cond) in fp32, then mod = W_mod s -------------------------
+__global__ __launch_bounds__(kThreads) void silu_cond_kernel(const uint16_t* __restrict__ cond,
+                                                             float* __restrict__ s, int n) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) s[i] = silu_f32(bf16_to_f32(cond[i]));
+}
+
+// One wavefront per output row; every item of the batch shares the weight read.
+__global__ __launch_bounds__(kThreads) void adaln_gemv_kernel(const float* __restrict__ s,
+                                                              const uint16_t* __restrict__ w,
+                                                              float* __restrict__ mod, int batch, int n_out,
+                                                              int d) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= n_out) return;
+  const u32x4* wr = reinterpret_cast<const u32x4*>(w + (size_t)row * d);
+  const int nch = d >> 3;
+  float acc[MOSS_MAX_BATCH];
+#pragma unroll
+  for (int b = 0; b < MOSS_MAX_BATCH; ++b) acc[b] = 0.0f;
+  for (int c = lane; c < nch; c += 64) {
+    float f[8];
+    unpack8(wr[c], f);
+#pragma unroll
+    for (int b = 0; b < MOSS_MAX_BATCH; ++b) {
+      if (b < batch) {
+        const f32x4* sp = reinterpret_cast<const f32x4*>(s + (size_t)b * d + 8 * c);
+        const f32x4 s0 = sp[0], s1 = sp[1];
+        acc[b] += f[0] * s0[0] + f[1] * s0[1] + f[2] * s0[2] + f[3] * s0[3] + f[4] * s1[0] +
+                  f[5] * s1[1] + f[6] * s1[2] + f[7] * s1[3];
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < MOSS_MAX_BATCH; ++b) {
+    if (b < batch) {
+      const float t = wave_sum(acc[b]);
+      if (lane == 0) mod[(size_t)b * n_out + row] = t;
+    }
+  }
+}
+
+// ---- a2/a8: modulated RMSNorm, one wavefront per row ------------------------
+// Row values stay in registers between the mean-square pass and the scaling
+// pass (d_model <= 8192 means at most 16 chunks per lane).
+constexpr int kMaxChunksPerLane = MOSS_MAX_DMODEL / 8 / 64;
+
+__global__ __launch_bounds__(kThreads) void mod_rmsnorm_kernel(const uint16_t* __restrict__ h,
+                                                               const float* __restrict__ shift,
+                                                               const float* __restrict__ scale,
+                                                               int mod_stride, uint16_t* __restrict__ out,
+                                                               int total_rows, int rows_per_item, int d,
+                                                               float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= total_rows) return;
+  const int b = row / rows_per_item;
+  const int nch = d >> 3;
+  const u32x4* src = reinterpret_cast<const u32x4*>(h + (size_t)row * d);
+  u32x4 v[kMaxChunksPerLane];
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kMaxChunksPerLane; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      v[i] = src[c];
+      float f[8];
+      unpack8(v[i], f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss += f[j] * f[j];
+    }
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+  const float* sh = shift + (size_t)b * mod_stride;
+  const float* sc = scale + (size_t)b * mod_stride;
+  u32x4* dst = reinterpret_cast<u32x4*>(out + (size_t)row * d);
+#pragma unroll
+  for (int i = 0; i < kMaxChunksPerLane; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      float f[8];
+      unpack8(v[i], f);
+      const f32x4 sh0 = reinterpret_cast<const f32x4*>(sh + 8 * c)[0];
+      const f32x4 sh1 = reinterpret_cast<const f32x4*>(sh + 8 * c)[1];
+      const f32x4 sc0 = reinterpret_cast<const f32x4*>(sc + 8 * c)[0];
+      const f32x4 sc1 = reinterpret_cast<const f32x4*>(sc + 8 * c)[1];
+      float o[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[j] = (f[j] * r) * (1.0f + sc0[j]) + sh0[j];
+        o[4 + j] = (f[4 + j] * r) * (1.0f + sc1[j]) + sh1[j];
+      }
+      dst[c] = pack8(o);
+    }
+  }
+}
+
+// ---- a7/a12: h += gate * y, in place ----------------------------------------
+__global__ __launch_bounds__(kThreads) void gated_add_kernel(u32x4* __restrict__ h, const float* __restrict__ gate,
+                                                             int gate_stride, const u32x4* __restrict__ y,
+                                                             int chunks_per_row, int rows_per_item, long total) {
+  for (long i = (long)blockIdx.x * kThreads + threadIdx.x; i < total; i += (long)gridDim.x * kThreads) {
+    const long row = i / chunks_per_row;
+    const int c = (int)(i - row * chunks_per_row);
+    const int b = (int)(row / rows_per_item);
+    const f32x4* g = reinterpret_cast<const f32x4*>(gate + (size_t)b * gate_stride + 8 * c);
+    const f32x4 g0 = g[0], g1 = g[1];
+    float hv[8], yv[8], o[8];
+    unpack8(h[i], hv);
+    unpack8(y[i], yv);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[j] = hv[j] + g0[j] * yv[j];
+      o[4 + j] = hv[4 + j] + g1[j] * yv[4 + j];
+    }
+    h[i] = pack8(o);
+  }
+}
+
+// ---- a10: z = SiLU(u_gate) * u_up -------------------------------------------
+__global__ __launch_bounds__(kThreads) void silu_mul_kernel(const uint16_t* __restrict__ u, u32x4* __restrict__ z,
+                                                            int f, long total) {
+  const int cpr = f >> 3;
+  for (long i = (long)blockIdx.x * kThreads + threadIdx.x; i < total; i += (long)gridDim.x * kThreads) {
+    const long row = i / cpr;
+    const int c = (int)(i - row * cpr);
+    const u32x4* ur = reinterpret_cast<const u32x4*>(u + (size_t)row * 2 * f);
+    float g[8], up[8], o[8];
+    unpack8(ur[c], g);
+    unpack8(ur[cpr + c], up);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = silu_f32(g[j]) * up[j];
+    z[i] = pack8(o);
+  }
+}
+
+// ---- rotary tables ------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void rope_build_kernel(int n_txt, int grid_w, double theta, float* rope,
+                                                              int rows) {
+  const int idx = blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= rows * 64) return;
+  const int t = idx >> 6, p = idx & 63;
+  double ang = 0.0;
+  if (t >= n_txt) {
+    const int g = t - n_txt;
+    const int y = g / grid_w, x = g - y * grid_w;
+    const double w = pow(theta, -(double)(p & 31) / 32.0);
+    ang = (double)(p < 32 ? y : x) * w;
+  }
+  rope[idx] = (float)cos(ang);
+  rope[(size_t)rows * 64 + idx] = (float)sin(ang);
+}
+
+int grid_for(long work, int per_block) {
+  long g = (work + per_block - 1) / per_block;
+  if (g > 65536L * 8) g = 65536L * 8;
+  return (int)(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+hipError_t launch_join_rows(const uint16_t* x, const uint16_t* txt, const ItemLens& lens, uint16_t* out,
+                            int batch, int n_txt, int n_img, int d, hipStream_t st) {
+  const long total = (long)batch * (n_txt + n_img) * (d / 8);
+  hipLaunchKernelGGL(join_rows_kernel, dim3(grid_for(total, kThreads)), dim3(kThreads), 0, st,
+                     reinterpret_cast<const u32x4*>(x), reinterpret_cast<const u32x4*>(txt), lens,
+                     reinterpret_cast<u32x4*>(out), n_txt, n_img, d / 8, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_cond(const uint16_t* cond, float* s, int batch, int d, hipStream_t st) {
+  const int n = batch * d;
+  hipLaunchKernelGGL(silu_cond_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, st, cond, s, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_adaln_gemv(const float* s, const uint16_t* w_mod, float* mod, int batch, int d, hipStream_t st) {
+  const int n_out = 6 * d;
+  hipLaunchKernelGGL(adaln_gemv_kernel, dim3((n_out + 3) / 4), dim3(kThreads), 0, st, s, w_mod, mod, batch,
+                     n_out, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_mod_rmsnorm(const uint16_t* h, const float* shift, const float* scale, int mod_stride,
+                              uint16_t* out, int batch, int rows, int d, float eps, hipStream_t st) {
+  const int total = batch * rows;
+  hipLaunchKernelGGL(mod_rmsnorm_kernel, dim3((total + 3) / 4), dim3(kThreads), 0, st, h, shift, scale,
+                     mod_stride, out, total, rows, d, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_gated_add(uint16_t* h, const float* gate, int gate_stride, const uint16_t* y, int batch,
+                            int rows, int d, hipStream_t st) {
+  const long total = (long)batch * rows * (d / 8);
+  hipLaunchKernelGGL(gated_add_kernel, dim3(grid_for(total, kThreads)), dim3(kThreads), 0, st,
+                     reinterpret_cast<u32x4*>(h), gate, gate_stride, reinterpret_cast<const u32x4*>(y), d / 8,
+                     rows, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_mul(const uint16_t* u, uint16_t* z, int rows, int f, hipStream_t st) {
+  const long total = (long)rows * (f / 8);
+  hipLaunchKernelGGL(silu_mul_kernel, dim3(grid_for(total, kThreads)), dim3(kThreads), 0, st, u,
+                     reinterpret_cast<u32x4*>(z), f, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_build(int n_txt, int grid_h, int grid_w, float theta, float* rope, hipStream_t st) {
+  const int rows = n_txt + grid_h * grid_w;
+  hipLaunchKernelGGL(rope_build_kernel, dim3((rows * 64 + kThreads - 1) / kThreads), dim3(kThreads), 0, st, n_txt,
+                     grid_w, (double)theta, rope, rows);
+  return hipGetLastError();
+}

@@ -1,0 +1,32 @@
+// Host-side launchers of the gfx950 kernels (one per step of the block).
+// Shapes are validated by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+struct ItemLens;
+
+hipError_t launch_join_rows(const uint16_t* x, const uint16_t* txt, const ItemLens& lens, uint16_t* out,
+                            int batch, int n_txt, int n_img, int d, hipStream_t st);
+hipError_t launch_silu_cond(const uint16_t* cond, float* s, int batch, int d, hipStream_t st);
+hipError_t launch_adaln_gemv(const float* s, const uint16_t* w_mod, float* mod, int batch, int d, hipStream_t st);
+hipError_t launch_mod_rmsnorm(const uint16_t* h, const float* shift, const float* scale, int mod_stride,
+                              uint16_t* out, int batch, int rows, int d, float eps, hipStream_t st);
+hipError_t launch_gated_add(uint16_t* h, const float* gate, int gate_stride, const uint16_t* y, int batch,
+                            int rows, int d, hipStream_t st);
+hipError_t launch_silu_mul(const uint16_t* u, uint16_t* z, int rows, int f, hipStream_t st);
+hipError_t launch_rope_build(int n_txt, int grid_h, int grid_w, float theta, float* rope, hipStream_t st);
+
+// c[m, n] = sum_k a[m, k] w[n, k]; n % 128 == 0, k % 64 == 0, strides % 8 == 0.
+hipError_t launch_gemm_nt(int m, int n, int k, const uint16_t* a, int lda, const uint16_t* w, int ldw,
+                          uint16_t* c, int ldc, hipStream_t st);
+
+// Rows of the packed attention layouts: rows rounded up to a multiple of 128.
+inline int packed_rows(int rows) { return (rows + 127) / 128 * 128; }
+
+hipError_t launch_qk_norm_rope_pack(int batch, int rows, int n_heads, float eps, const uint16_t* qkv,
+                                    const uint16_t* q_gain, const uint16_t* k_gain, const float* rope,
+                                    uint16_t* q, uint16_t* k, uint16_t* v, hipStream_t st);
+hipError_t launch_attention(int batch, int n_heads, int rows, int n_txt, const ItemLens& lens, const uint16_t* q,
+                            const uint16_t* k, const uint16_t* v, uint16_t* o, hipStream_t st);

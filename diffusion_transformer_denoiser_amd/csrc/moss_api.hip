@@ -1,0 +1,517 @@
+// The C ABI of libmoss.so (declared in include/moss.h): argument validation,
+// workspace planning, the launch sequence of one block and of a stack, status
+// strings and the timing probe.  No function here allocates device memory.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "launch.h"
+#include "moss.h"
+
+namespace {
+
+thread_local std::string g_hip_error;
+
+int hip_fail(hipError_t e, const char* what) {
+  char buf[256];
+  snprintf(buf, sizeof(buf), "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+  g_hip_error = buf;
+  return MOSS_EHIP;
+}
+
+#define MOSS_TRY(expr, what)                  \
+  do {                                        \
+    hipError_t e_ = (expr);                   \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---- geometry ----------------------------------------------------------------
+bool dims_ok(const moss_dims* d) {
+  if (!d) return false;
+  if (d->batch < 1 || d->batch > MOSS_MAX_BATCH) return false;
+  if (d->n_img < 0 || d->n_txt < 0) return false;
+  const long t = (long)d->n_txt + d->n_img;
+  if (t < 1 || t > MOSS_MAX_ROWS) return false;
+  if (d->head_dim != MOSS_HEAD_DIM || d->n_heads < 1) return false;
+  if ((long)d->d_model != (long)d->n_heads * MOSS_HEAD_DIM || d->d_model > MOSS_MAX_DMODEL) return false;
+  if (d->mlp_inner < 128 || d->mlp_inner % 128 != 0 || d->mlp_inner > 8 * MOSS_MAX_DMODEL) return false;
+  if (!(d->eps > 0.0f) || !isfinite(d->eps)) return false;
+  return true;
+}
+
+bool lens_ok(const moss_dims* d, const int32_t* txt_len, ItemLens* out) {
+  for (int b = 0; b < MOSS_MAX_BATCH; ++b) out->len[b] = 0;
+  for (int b = 0; b < d->batch; ++b) {
+    const int32_t n = txt_len ? txt_len[b] : d->n_txt;
+    if (n < 0 || n > d->n_txt || (long)n + d->n_img < 1) return false;
+    out->len[b] = n;
+  }
+  return true;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t s_cond, mod, a, y, qkv, qp, kp, vp, u, z, total;
+};
+
+// Offsets (bytes) into the workspace.  a holds the first norm's output, then
+// the attention output, then the second norm's output; y holds each
+// projection output that is added to the residual; the union region holds the
+// qkv rows and packed q/k/v during attention, and the MLP activations after.
+Layout plan(const moss_dims* d) {
+  Layout L;
+  const size_t B = d->batch, T = (size_t)d->n_txt + d->n_img, D = d->d_model, F = d->mlp_inner;
+  const size_t R = B * T, Tp = packed_rows((int)T), H = d->n_heads;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += round256(bytes);
+    return o;
+  };
+  L.s_cond = take(4 * B * D);
+  L.mod = take(4 * B * 6 * D);
+  L.a = take(2 * R * D);
+  L.y = take(2 * R * D);
+  const size_t base = off;
+  const size_t packed = round256(2 * B * H * Tp * 128);
+  L.qkv = base;
+  L.qp = base + round256(2 * R * 3 * D);
+  L.kp = L.qp + packed;
+  L.vp = L.kp + packed;
+  const size_t end1 = L.vp + packed;
+  L.u = base;
+  L.z = base + round256(2 * R * 2 * F);
+  const size_t end2 = L.z + round256(2 * R * F);
+  L.total = end1 > end2 ? end1 : end2;
+  return L;
+}
+
+// byte range [p, p + n) overlaps [q, q + m)
+bool overlaps(const void* p, size_t n, const void* q, size_t m) {
+  if (!p || !q || n == 0 || m == 0) return false;
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + m && b < a + n;
+}
+
+// ---- device capability cache ---------------------------------------------------
+std::mutex g_dev_mu;
+std::vector<int> g_dev_state;  // 0 unknown, 1 gfx950, 2 other
+
+int check_device(int dev) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0 || dev < 0 || dev >= count) return MOSS_EDEVICE;
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if ((int)g_dev_state.size() < count) g_dev_state.resize(count, 0);
+    if (g_dev_state[dev] == 1) return MOSS_OK;
+    if (g_dev_state[dev] == 2) return MOSS_EDEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOSS_EDEVICE;
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  g_dev_state[dev] = ok ? 1 : 2;
+  return ok ? MOSS_OK : MOSS_EDEVICE;
+}
+
+int check_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOSS_EDEVICE;
+  return check_device(dev);
+}
+
+// ---- timing probe -------------------------------------------------------------------
+struct Probe {
+  std::mutex mu;
+  int step = -1;
+  int max = 0;
+  int used = 0;
+  std::vector<hipEvent_t> ev;  // 2 per launch
+};
+Probe g_probe;
+
+// Records the start event of a probed launch; returns its slot or -1.
+int probe_begin(int step, hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_probe.mu);
+  if (g_probe.step != step || g_probe.used >= g_probe.max) return -1;
+  const int slot = g_probe.used;
+  if (hipEventRecord(g_probe.ev[2 * slot], st) != hipSuccess) return -1;
+  g_probe.used = slot + 1;
+  return slot;
+}
+void probe_end(int slot, hipStream_t st) {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lk(g_probe.mu);
+  (void)hipEventRecord(g_probe.ev[2 * slot + 1], st);
+}
+
+struct StepTimer {
+  int slot;
+  hipStream_t st;
+  StepTimer(int step, hipStream_t s) : slot(probe_begin(step, s)), st(s) {}
+  ~StepTimer() { probe_end(slot, st); }
+};
+
+// ---- the block ----------------------------------------------------------------------
+struct Ctx {
+  const moss_dims* d;
+  ItemLens lens;
+  Layout L;
+  char* ws;
+  hipStream_t st;
+};
+
+int run_block(const Ctx& c, const moss_block_weights* w, const float* rope, uint16_t* h) {
+  const moss_dims* d = c.d;
+  const int B = d->batch, T = d->n_txt + d->n_img, D = d->d_model, F = d->mlp_inner, H = d->n_heads;
+  const int R = B * T;
+  float* s = reinterpret_cast<float*>(c.ws + c.L.s_cond);
+  float* mod = reinterpret_cast<float*>(c.ws + c.L.mod);
+  uint16_t* a = reinterpret_cast<uint16_t*>(c.ws + c.L.a);
+  uint16_t* y = reinterpret_cast<uint16_t*>(c.ws + c.L.y);
+  uint16_t* qkv = reinterpret_cast<uint16_t*>(c.ws + c.L.qkv);
+  uint16_t* qp = reinterpret_cast<uint16_t*>(c.ws + c.L.qp);
+  uint16_t* kp = reinterpret_cast<uint16_t*>(c.ws + c.L.kp);
+  uint16_t* vp = reinterpret_cast<uint16_t*>(c.ws + c.L.vp);
+  uint16_t* u = reinterpret_cast<uint16_t*>(c.ws + c.L.u);
+  uint16_t* z = reinterpret_cast<uint16_t*>(c.ws + c.L.z);
+  const int ms = 6 * D;  // item stride of the modulation vector
+  hipStream_t st = c.st;
+  {
+    StepTimer t(MOSS_STEP_ADALN, st);
+    MOSS_TRY(launch_adaln_gemv(s, w->w_mod, mod, B, D, st), "adaln_gemv");
+  }
+  {
+    StepTimer t(MOSS_STEP_NORM1, st);
+    MOSS_TRY(launch_mod_rmsnorm(h, mod + 0 * D, mod + 1 * D, ms, a, B, T, D, d->eps, st), "mod_rmsnorm");
+  }
+  {
+    StepTimer t(MOSS_STEP_QKV, st);
+    MOSS_TRY(launch_gemm_nt(R, 3 * D, D, a, D, w->w_qkv, D, qkv, 3 * D, st), "gemm qkv");
+  }
+  {
+    StepTimer t(MOSS_STEP_QKNORM, st);
+    MOSS_TRY(launch_qk_norm_rope_pack(B, T, H, d->eps, qkv, w->q_gain, w->k_gain, rope, qp, kp, vp, st),
+             "qk_norm_rope_pack");
+  }
+  {
+    StepTimer t(MOSS_STEP_ATTN, st);
+    MOSS_TRY(launch_attention(B, H, T, d->n_txt, c.lens, qp, kp, vp, a, st), "attention");
+  }
+  {
+    StepTimer t(MOSS_STEP_OUT, st);
+    MOSS_TRY(launch_gemm_nt(R, D, D, a, D, w->w_out, D, y, D, st), "gemm out");
+  }
+  {
+    StepTimer t(MOSS_STEP_GATE1, st);
+    MOSS_TRY(launch_gated_add(h, mod + 2 * D, ms, y, B, T, D, st), "gated_add");
+  }
+  {
+    StepTimer t(MOSS_STEP_NORM2, st);
+    MOSS_TRY(launch_mod_rmsnorm(h, mod + 3 * D, mod + 4 * D, ms, a, B, T, D, d->eps, st), "mod_rmsnorm");
+  }
+  {
+    StepTimer t(MOSS_STEP_UP, st);
+    MOSS_TRY(launch_gemm_nt(R, 2 * F, D, a, D, w->w_up, D, u, 2 * F, st), "gemm up");
+  }
+  {
+    StepTimer t(MOSS_STEP_SILU, st);
+    MOSS_TRY(launch_silu_mul(u, z, R, F, st), "silu_mul");
+  }
+  {
+    StepTimer t(MOSS_STEP_DOWN, st);
+    MOSS_TRY(launch_gemm_nt(R, D, F, z, F, w->w_down, F, y, D, st), "gemm down");
+  }
+  {
+    StepTimer t(MOSS_STEP_GATE2, st);
+    MOSS_TRY(launch_gated_add(h, mod + 5 * D, ms, y, B, T, D, st), "gated_add");
+  }
+  return MOSS_OK;
+}
+
+bool weights_ok(const moss_block_weights* w) {
+  if (!w) return false;
+  const void* p[] = {w->w_mod, w->w_qkv, w->q_gain, w->k_gain, w->w_out, w->w_up, w->w_down};
+  for (const void* q : p)
+    if (!q || !aligned16(q)) return false;
+  return true;
+}
+
+// Validation shared by the block and the stack; fills ctx on success.
+int validate_forward(const moss_dims* d, int n_blocks, const uint16_t* x, const uint16_t* txt,
+                     const int32_t* txt_len, const uint16_t* cond, const moss_block_weights* blocks,
+                     const float* rope, uint16_t* out, void* workspace, size_t ws_bytes, Ctx* ctx) {
+  if (!dims_ok(d) || n_blocks < 1 || !blocks) return MOSS_EINVAL;
+  if (!cond || !rope || !out || !aligned16(cond) || !aligned16(rope) || !aligned16(out)) return MOSS_EINVAL;
+  if (d->n_img > 0 && (!x || !aligned16(x))) return MOSS_EINVAL;
+  if (d->n_txt > 0 && (!txt || !aligned16(txt))) return MOSS_EINVAL;
+  if (!lens_ok(d, txt_len, &ctx->lens)) return MOSS_EINVAL;
+  for (int i = 0; i < n_blocks; ++i)
+    if (!weights_ok(&blocks[i])) return MOSS_EINVAL;
+  if (!workspace || !aligned16(workspace)) return MOSS_EWORKSPACE;
+  ctx->L = plan(d);
+  if (ws_bytes < ctx->L.total) return MOSS_EWORKSPACE;
+  const size_t B = d->batch, T = (size_t)d->n_txt + d->n_img, D = d->d_model, F = d->mlp_inner;
+  const size_t out_bytes = 2 * B * T * D;
+  if (overlaps(out, out_bytes, x, 2 * B * d->n_img * D) || overlaps(out, out_bytes, txt, 2 * B * d->n_txt * D) ||
+      overlaps(out, out_bytes, cond, 2 * B * D) || overlaps(out, out_bytes, rope, 4 * 2 * T * 64) ||
+      overlaps(out, out_bytes, workspace, ctx->L.total))
+    return MOSS_EALIAS;
+  for (int i = 0; i < n_blocks; ++i) {
+    const moss_block_weights& w = blocks[i];
+    if (overlaps(out, out_bytes, w.w_mod, 2 * 6 * D * D) || overlaps(out, out_bytes, w.w_qkv, 2 * 3 * D * D) ||
+        overlaps(out, out_bytes, w.q_gain, 256) || overlaps(out, out_bytes, w.k_gain, 256) ||
+        overlaps(out, out_bytes, w.w_out, 2 * D * D) || overlaps(out, out_bytes, w.w_up, 2 * 2 * F * D) ||
+        overlaps(out, out_bytes, w.w_down, 2 * D * F))
+      return MOSS_EALIAS;
+  }
+  ctx->d = d;
+  ctx->ws = static_cast<char*>(workspace);
+  return MOSS_OK;
+}
+
+int forward(const moss_dims* d, int n_blocks, const uint16_t* x, const uint16_t* txt, const int32_t* txt_len,
+            const uint16_t* cond, const moss_block_weights* blocks, const float* rope, uint16_t* out,
+            void* workspace, size_t ws_bytes, hipStream_t st) {
+  Ctx c;
+  int rc = validate_forward(d, n_blocks, x, txt, txt_len, cond, blocks, rope, out, workspace, ws_bytes, &c);
+  if (rc != MOSS_OK) return rc;
+  rc = check_current_device();
+  if (rc != MOSS_OK) return rc;
+  c.st = st;
+  {
+    StepTimer t(MOSS_STEP_JOIN, st);
+    MOSS_TRY(launch_join_rows(x, txt, c.lens, out, d->batch, d->n_txt, d->n_img, d->d_model, st), "join_rows");
+  }
+  MOSS_TRY(launch_silu_cond(cond, reinterpret_cast<float*>(c.ws + c.L.s_cond), d->batch, d->d_model, st),
+           "silu_cond");
+  for (int i = 0; i < n_blocks; ++i) {
+    rc = run_block(c, &blocks[i], rope, out);
+    if (rc != MOSS_OK) return rc;
+  }
+  return MOSS_OK;
+}
+
+int single_device_check() { return check_current_device(); }
+
+}  // namespace
+
+// ============================================================================
+// exported C ABI
+// ============================================================================
+extern "C" {
+
+const char* moss_status_string(int status) {
+  switch (status) {
+    case MOSS_OK: return "ok";
+    case MOSS_EINVAL: return "invalid argument";
+    case MOSS_EALIAS: return "an output overlaps an input or the workspace";
+    case MOSS_EWORKSPACE: return "workspace missing or too small";
+    case MOSS_EDEVICE: return "no gfx950 device";
+    case MOSS_EHIP: return g_hip_error.empty() ? "HIP error" : g_hip_error.c_str();
+    default: return "unknown status";
+  }
+}
+
+int moss_device_check(int hip_device) { return check_device(hip_device); }
+
+size_t moss_workspace_bytes(const moss_dims* dims, int32_t n_blocks) {
+  if (!dims_ok(dims) || n_blocks < 1) return 0;
+  return plan(dims).total;
+}
+
+int32_t moss_packed_rows(int32_t rows) { return rows < 1 ? 0 : packed_rows(rows); }
+
+int moss_rope_build(int32_t n_txt, int32_t grid_h, int32_t grid_w, float theta, float* rope, hipStream_t stream) {
+  if (n_txt < 0 || grid_h < 1 || grid_w < 1 || !(theta > 1.0f) || !isfinite(theta)) return MOSS_EINVAL;
+  if ((long)n_txt + (long)grid_h * grid_w > MOSS_MAX_ROWS) return MOSS_EINVAL;
+  if (!rope || !aligned16(rope)) return MOSS_EINVAL;
+  const int rc = single_device_check();
+  if (rc != MOSS_OK) return rc;
+  MOSS_TRY(launch_rope_build(n_txt, grid_h, grid_w, theta, rope, stream), "rope_build");
+  return MOSS_OK;
+}
+
+int moss_block_forward(const moss_dims* dims, const uint16_t* x, const uint16_t* txt, const int32_t* txt_len,
+                       const uint16_t* cond, const moss_block_weights* w, const float* rope, uint16_t* out,
+                       void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return forward(dims, 1, x, txt, txt_len, cond, w, rope, out, workspace, ws_bytes, stream);
+}
+
+int moss_stack_forward(const moss_dims* dims, int32_t n_blocks, const uint16_t* x, const uint16_t* txt,
+                       const int32_t* txt_len, const uint16_t* cond, const moss_block_weights* blocks,
+                       const float* rope, uint16_t* out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return forward(dims, n_blocks, x, txt, txt_len, cond, blocks, rope, out, workspace, ws_bytes, stream);
+}
+
+int moss_k_join_rows(int32_t batch, int32_t n_txt, int32_t n_img, int32_t d_model, const uint16_t* x,
+                     const uint16_t* txt, const int32_t* txt_len, uint16_t* out, hipStream_t stream) {
+  moss_dims d = {batch, n_img, n_txt, d_model, d_model / MOSS_HEAD_DIM, MOSS_HEAD_DIM, 128, 1e-6f};
+  if (!dims_ok(&d)) return MOSS_EINVAL;
+  ItemLens lens;
+  if (!lens_ok(&d, txt_len, &lens)) return MOSS_EINVAL;
+  if (!out || !aligned16(out) || (n_img > 0 && (!x || !aligned16(x))) || (n_txt > 0 && (!txt || !aligned16(txt))))
+    return MOSS_EINVAL;
+  const size_t ob = 2ull * batch * (n_txt + n_img) * d_model;
+  if (overlaps(out, ob, x, 2ull * batch * n_img * d_model) || overlaps(out, ob, txt, 2ull * batch * n_txt * d_model))
+    return MOSS_EALIAS;
+  const int rc = single_device_check();
+  if (rc != MOSS_OK) return rc;
+  MOSS_TRY(launch_join_rows(x, txt, lens, out, batch, n_txt, n_img, d_model, stream), "join_rows");
+  return MOSS_OK;
+}
+
+int moss_k_adaln_gemv(int32_t batch, int32_t d_model, const uint16_t* cond, const uint16_t* w_mod, float* mod,
+                      void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (batch < 1 || batch > MOSS_MAX_BATCH || d_model < 128 || d_model % 128 || d_model > MOSS_MAX_DMODEL)
+    return MOSS_EINVAL;
+  if (!cond || !w_mod || !mod || !aligned16(cond) || !aligned16(w_mod) || !aligned16(mod)) return MOSS_EINVAL;
+  if (!workspace || !aligned16(workspace) || ws_bytes < 4ull * batch * d_model) return MOSS_EWORKSPACE;
+  if (overlaps(mod, 4ull * batch * 6 * d_model, workspace, 4ull * batch * d_model)) return MOSS_EALIAS;
+  const int rc = single_device_check();
+  if (rc != MOSS_OK) return rc;
+  float* s = static_cast<float*>(workspace);
+  MOSS_TRY(launch_silu_cond(cond, s, batch, d_model, stream), "silu_cond");
+  MOSS_TRY(launch_adaln_gemv(s, w_mod, mod, batch, d_model, stream), "adaln_gemv");
+  return MOSS_OK;
+}
+
+int moss_k_mod_rmsnorm(int32_t batch, int32_t rows, int32_t d_model, float eps, const uint16_t* h,
+                       const float* shift, const float* scale, int32_t mod_stride, uint16_t* out,
+                       hipStream_t stream) {
+  if (batch < 1 || rows < 1 || (long)batch * rows > (long)MOSS_MAX_BATCH * MOSS_MAX_ROWS) return MOSS_EINVAL;
+  if (d_model < 128 || d_model % 128 || d_model > MOSS_MAX_DMODEL || !(eps > 0.0f) || !isfinite(eps))
+    return MOSS_EINVAL;
+  if (mod_stride < d_model || mod_stride % 4) return MOSS_EINVAL;
+  if (!h || !shift || !scale || !out || !aligned16(h) || !aligned16(shift) || !aligned16(scale) || !aligned16(out))
+    return MOSS_EINVAL;
+  if (overlaps(out, 2ull * batch * rows * d_model, h, 2ull * batch * rows * d_model)) return MOSS_EALIAS;
+  const int rc = single_device_check();
+  if (rc != MOSS_OK) return rc;
+  MOSS_TRY(launch_mod_rmsnorm(h, shift, scale, mod_stride, out, batch, rows, d_model, eps, stream), "mod_rmsnorm");
+  return MOSS_OK;
+}
+
+int moss_k_gemm_nt(int32_t m, int32_t n, int32_t k, const uint16_t* a, int32_t lda, const uint16_t* w,
+                   int32_t ldw, uint16_t* c, int32_t ldc, hipStream_t stream) {
+  if (m < 1 || n < 128 || k < 128 || n % 128 || k % 128) return MOSS_EINVAL;
+  if (lda < k || ldw < k || ldc < n || lda % 8 || ldw % 8 || ldc % 8) return MOSS_EINVAL;
+  if ((long)m > (long)MOSS_MAX_BATCH * MOSS_MAX_ROWS) return MOSS_EINVAL;
+  if (!a || !w || !c || !aligned16(a) || !aligned16(w) || !aligned16(c)) return MOSS_EINVAL;
+  const size_t cb = 2ull * ((size_t)(m - 1) * ldc + n);
+  if (overlaps(c, cb, a, 2ull * ((size_t)(m - 1) * lda + k)) || overlaps(c, cb, w, 2ull * ((size_t)(n - 1) * ldw + k)))
+    return MOSS_EALIAS;
+  const int rc = single_device_check();
+  if (rc != MOSS_OK) return rc;
+  MOSS_TRY(launch_gemm_nt(m, n, k, a, lda, w, ldw, c, ldc, stream), "gemm_nt");
+  return MOSS_OK;
+}
+
+int moss_k_qk_norm_rope_pack(int32_t batch, int32_t rows, int32_t n_heads, float eps, const uint16_t* qkv,
+                             const uint16_t* q_gain, const uint16_t* k_gain, const float* rope, uint16_t* q,
+                             uint16_t* k, uint16_t* v, hipStream_t stream) {
+  if (batch < 1 || batch > MOSS_MAX_BATCH || rows < 1 || rows > MOSS_MAX_ROWS || n_heads < 1 ||
+      n_heads * MOSS_HEAD_DIM > MOSS_MAX_DMODEL || !(eps > 0.0f) || !isfinite(eps))
+    return MOSS_EINVAL;
+  const void* p[] = {qkv, q_gain, k_gain, rope, q, k, v};
+  for (const void* x : p)
+    if (!x || !aligned16(x)) return MOSS_EINVAL;
+  const size_t pk = 2ull * batch * n_heads * packed_rows(rows) * 128;
+  const size_t in = 2ull * batch * rows * 3 * n_heads * 128;
+  if (overlaps(q, pk, qkv, in) || overlaps(k, pk, qkv, in) || overlaps(v, pk, qkv, in) || overlaps(q, pk, k, pk) ||
+      overlaps(q, pk, v, pk) || overlaps(k, pk, v, pk))
+    return MOSS_EALIAS;
+  const int rc = single_device_check();
+  if (rc != MOSS_OK) return rc;
+  MOSS_TRY(launch_qk_norm_rope_pack(batch, rows, n_heads, eps, qkv, q_gain, k_gain, rope, q, k, v, stream),
+           "qk_norm_rope_pack");
+  return MOSS_OK;
+}
+
+int moss_k_attention(int32_t batch, int32_t n_heads, int32_t rows, int32_t n_txt, const int32_t* txt_len,
+                     const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, hipStream_t stream) {
+  moss_dims d = {batch, rows - n_txt, n_txt, n_heads * MOSS_HEAD_DIM, n_heads, MOSS_HEAD_DIM, 128, 1e-6f};
+  if (n_txt < 0 || n_txt > rows || !dims_ok(&d)) return MOSS_EINVAL;
+  ItemLens lens;
+  if (!lens_ok(&d, txt_len, &lens)) return MOSS_EINVAL;
+  const void* p[] = {q, k, v, o};
+  for (const void* x : p)
+    if (!x || !aligned16(x)) return MOSS_EINVAL;
+  const size_t pk = 2ull * batch * n_heads * packed_rows(rows) * 128;
+  const size_t ob = 2ull * batch * rows * n_heads * 128;
+  if (overlaps(o, ob, q, pk) || overlaps(o, ob, k, pk) || overlaps(o, ob, v, pk)) return MOSS_EALIAS;
+  const int rc = single_device_check();
+  if (rc != MOSS_OK) return rc;
+  MOSS_TRY(launch_attention(batch, n_heads, rows, n_txt, lens, q, k, v, o, stream), "attention");
+  return MOSS_OK;
+}
+
+int moss_k_silu_mul(int32_t rows, int32_t mlp_inner, const uint16_t* u, uint16_t* z, hipStream_t stream) {
+  if (rows < 1 || (long)rows > (long)MOSS_MAX_BATCH * MOSS_MAX_ROWS || mlp_inner < 128 || mlp_inner % 128)
+    return MOSS_EINVAL;
+  if (!u || !z || !aligned16(u) || !aligned16(z)) return MOSS_EINVAL;
+  if (overlaps(z, 2ull * rows * mlp_inner, u, 4ull * rows * mlp_inner)) return MOSS_EALIAS;
+  const int rc = single_device_check();
+  if (rc != MOSS_OK) return rc;
+  MOSS_TRY(launch_silu_mul(u, z, rows, mlp_inner, stream), "silu_mul");
+  return MOSS_OK;
+}
+
+int moss_k_gated_add(int32_t batch, int32_t rows, int32_t d_model, uint16_t* h, const float* gate,
+                     int32_t gate_stride, const uint16_t* y, hipStream_t stream) {
+  if (batch < 1 || batch > MOSS_MAX_BATCH || rows < 1 || rows > MOSS_MAX_ROWS || d_model < 128 || d_model % 128 ||
+      d_model > MOSS_MAX_DMODEL || gate_stride < d_model || gate_stride % 4)
+    return MOSS_EINVAL;
+  if (!h || !gate || !y || !aligned16(h) || !aligned16(gate) || !aligned16(y)) return MOSS_EINVAL;
+  const size_t hb = 2ull * batch * rows * d_model;
+  if (overlaps(h, hb, y, hb) || overlaps(h, hb, gate, 4ull * ((size_t)(batch - 1) * gate_stride + d_model)))
+    return MOSS_EALIAS;
+  const int rc = single_device_check();
+  if (rc != MOSS_OK) return rc;
+  MOSS_TRY(launch_gated_add(h, gate, gate_stride, y, batch, rows, d_model, stream), "gated_add");
+  return MOSS_OK;
+}
+
+int moss_probe_arm(int32_t step, int32_t max_launches) {
+  if (step < 0 || step >= MOSS_NUM_STEPS || max_launches < 1 || max_launches > 4096) return MOSS_EINVAL;
+  std::lock_guard<std::mutex> lk(g_probe.mu);
+  while ((int)g_probe.ev.size() < 2 * max_launches) {
+    hipEvent_t e;
+    const hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) return hip_fail(err, "hipEventCreate");
+    g_probe.ev.push_back(e);
+  }
+  g_probe.step = step;
+  g_probe.max = max_launches;
+  g_probe.used = 0;
+  return MOSS_OK;
+}
+
+int32_t moss_probe_collect(float* ms, int32_t max_out) {
+  if (max_out < 0 || (max_out > 0 && !ms)) return -MOSS_EINVAL;
+  std::lock_guard<std::mutex> lk(g_probe.mu);
+  const int n = g_probe.used;
+  g_probe.step = -1;
+  g_probe.used = 0;
+  for (int i = 0; i < n; ++i) {
+    hipError_t e = hipEventSynchronize(g_probe.ev[2 * i + 1]);
+    if (e != hipSuccess) return -hip_fail(e, "hipEventSynchronize");
+    if (i < max_out) {
+      float t = 0.0f;
+      e = hipEventElapsedTime(&t, g_probe.ev[2 * i], g_probe.ev[2 * i + 1]);
+      if (e != hipSuccess) return -hip_fail(e, "hipEventElapsedTime");
+      ms[i] = t;
+    }
+  }
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// a4: per (row, head) RMSNorm of q and k over the 128 head dims, times the
+// q/k gain, then the rotary rotation of interleaved pairs; v copied.  The
+// results are written in the packed layouts the attention kernel reads
+// (see moss.h): Q and K row-major per (item, head), V transposed per 64-key
+// tile with the keys of each 16-key group in the order 0-3, 8-11, 4-7, 12-15,
+// so that one 16-byte LDS read gives a lane the eight keys its MFMA operand
+// needs.
+//
+// The MOSS-Image transformer page (TensorFold PR #1528, "What it adds") names
+// this kernel "q/k norm and rotary into packed rows".
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kTok = 64;      // tokens per workgroup
+constexpr int kThreads = 256; // 16 groups of 16 lanes; a group owns one 128-dim row
+constexpr int kVPitch = 136;  // LDS row pitch (bf16) of the V staging tile
+
+__device__ __forceinline__ int vperm(int p) {
+  // position within a 16-key group -> key (an involution: swap the middle quads)
+  const int q = (p >> 2) & 3;
+  const int qq = (q == 1) ? 2 : (q == 2 ? 1 : q);
+  return (p & ~15) | (qq << 2) | (p & 3);
+}
+
+__global__ __launch_bounds__(kThreads) void qk_norm_rope_pack_kernel(
+    const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_gain, const uint16_t* __restrict__ k_gain,
+    const float* __restrict__ rope, uint16_t* __restrict__ qo, uint16_t* __restrict__ ko, uint16_t* __restrict__ vo,
+    int rows, int rows_pad, int n_heads, float eps) {
+  __shared__ uint16_t vs[kTok * kVPitch];
+  const int tile = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
+  const int t0 = tile * kTok;
+  const int d = n_heads * 128;
+  const int tid = threadIdx.x;
+  const int grp = tid >> 4, j = tid & 15;
+  const size_t bh = (size_t)b * n_heads + head;
+
+  float gq[8], gk[8];
+  unpack8(reinterpret_cast<const u32x4*>(q_gain)[j], gq);
+  unpack8(reinterpret_cast<const u32x4*>(k_gain)[j], gk);
+
+  // q and k: 128 rows (64 tokens x {q, k}), 16 per pass
+#pragma unroll 1
+  for (int it = 0; it < 8; ++it) {
+    const int rr = it * 16 + grp;
+    const int which = rr >> 6;  // 0 = q, 1 = k
+    const int t = t0 + (rr & 63);
+    float f[8];
+    float ss = 0.0f;
+    if (t < rows) {
+      const uint16_t* src = qkv + ((size_t)b * rows + t) * 3 * d + which * d + head * 128;
+      unpack8(reinterpret_cast<const u32x4*>(src)[j], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = 0.0f;
+    }
+    ss = group_sum<16>(ss);
+    u32x4 res = {0u, 0u, 0u, 0u};
+    if (t < rows) {
+      const float r = 1.0f / sqrtf(ss / 128.0f + eps);
+      const float* g = which ? gk : gq;
+      const f32x4 c4 = reinterpret_cast<const f32x4*>(rope + (size_t)t * 64)[j];
+      const f32x4 s4 = reinterpret_cast<const f32x4*>(rope + (size_t)rows * 64 + (size_t)t * 64)[j];
+      float o[8];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float x0 = (f[2 * p] * r) * g[2 * p];
+        const float x1 = (f[2 * p + 1] * r) * g[2 * p + 1];
+        o[2 * p] = x0 * c4[p] - x1 * s4[p];
+        o[2 * p + 1] = x0 * s4[p] + x1 * c4[p];
+      }
+      res = pack8(o);
+    }
+    uint16_t* dst = (which ? ko : qo) + (bh * rows_pad + t) * 128;
+    reinterpret_cast<u32x4*>(dst)[j] = res;
+  }
+
+  // v: stage the 64 x 128 tile in LDS, then write it transposed
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = tid + kThreads * i;  // 1024 chunks: token = id / 16, chunk = id % 16
+    const int tk = id >> 4, c = id & 15;
+    const int t = t0 + tk;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (t < rows) v = reinterpret_cast<const u32x4*>(qkv + ((size_t)b * rows + t) * 3 * d + 2 * d + head * 128)[c];
+    *reinterpret_cast<u32x4*>(&vs[tk * kVPitch + c * 8]) = v;
+  }
+  __syncthreads();
+  uint16_t* vt = vo + (bh * (rows_pad / kTok) + tile) * (kTok * 128);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = tid + kThreads * i;  // 1024 chunks: dim = id / 8, positions 8*(id % 8) .. +7
+    const int dim = id >> 3, pc = id & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k0 = vperm(pc * 8 + 2 * e), k1 = vperm(pc * 8 + 2 * e + 1);
+      w[e] = (uint32_t)vs[k0 * kVPitch + dim] | ((uint32_t)vs[k1 * kVPitch + dim] << 16);
+    }
+    u32x4 out = {w[0], w[1], w[2], w[3]};
+    reinterpret_cast<u32x4*>(vt)[id] = out;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_qk_norm_rope_pack(int batch, int rows, int n_heads, float eps, const uint16_t* qkv,
+                                    const uint16_t* q_gain, const uint16_t* k_gain, const float* rope,
+                                    uint16_t* q, uint16_t* k, uint16_t* v, hipStream_t st) {
+  const int rp = packed_rows(rows);
+  hipLaunchKernelGGL(qk_norm_rope_pack_kernel, dim3(rp / kTok, n_heads, batch), dim3(kThreads), 0, st, qkv, q_gain,
+                     k_gain, rope, q, k, v, rows, rp, n_heads, eps);
+  return hipGetLastError();
+}

@@ -154,18 +154,25 @@ def make_activations(geom: Geometry, seed: int = 0) -> dict:
     return {"x": x, "txt": txt, "txt_len": lens, "cond": cond}
 
 
-def make_block_weights(geom: Geometry, seed: int = 0, block: int = 0) -> dict:
-    """Weights of one block as bf16 bits; projection matrices are row-major [out, in]."""
+def make_block_weights(geom: Geometry, seed: int = 0, block: int = 0, std: float = WEIGHT_STD,
+                       gain_std: float = WEIGHT_STD, gain_mean: float = 1.0) -> dict:
+    """Weights of one block as bf16 bits; projection matrices are row-major [out, in].
+
+    ``std`` defaults to the workloads' N(0, 0.02).  A small geometry drawn with
+    ``std = 0.02 * sqrt(3072 / d_model)`` has the same branch magnitudes as the
+    D = 3072 block (each projection output's spread scales with std * sqrt(D)).
+    ``gain_mean`` scales the q/k gains (4.0 makes the logits about N(0, 16)).
+    """
     d, f, hd = geom.d_model, geom.mlp_inner, geom.head_dim
     k = 1 + block
     return {
-        "w_mod": normal_bf16(seed, (k, 0), (6 * d, d), WEIGHT_STD),
-        "w_qkv": normal_bf16(seed, (k, 1), (3 * d, d), WEIGHT_STD),
-        "q_gain": normal_bf16(seed, (k, 2), (hd,), WEIGHT_STD, offset=1.0),
-        "k_gain": normal_bf16(seed, (k, 3), (hd,), WEIGHT_STD, offset=1.0),
-        "w_out": normal_bf16(seed, (k, 4), (d, d), WEIGHT_STD),
-        "w_up": normal_bf16(seed, (k, 5), (2 * f, d), WEIGHT_STD),
-        "w_down": normal_bf16(seed, (k, 6), (d, f), WEIGHT_STD),
+        "w_mod": normal_bf16(seed, (k, 0), (6 * d, d), std),
+        "w_qkv": normal_bf16(seed, (k, 1), (3 * d, d), std),
+        "q_gain": normal_bf16(seed, (k, 2), (hd,), gain_std, offset=gain_mean),
+        "k_gain": normal_bf16(seed, (k, 3), (hd,), gain_std, offset=gain_mean),
+        "w_out": normal_bf16(seed, (k, 4), (d, d), std),
+        "w_up": normal_bf16(seed, (k, 5), (2 * f, d), std),
+        "w_down": normal_bf16(seed, (k, 6), (d, f), std),
     }
 
 

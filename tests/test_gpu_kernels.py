@@ -1,0 +1,262 @@
+"""Per-step parity of the HIP kernels against the float64 oracle (GPU).
+
+Every kernel is called through the C ABI on seeded inputs and compared
+element by element with the oracle's matching step on the same bf16 bits.
+Sizes span several tiles and a ragged tail.
+"""
+import numpy as np
+import pytest
+
+from diffusion_transformer_denoiser_amd import moss, synth
+from oracle import dit_block as ob
+
+from . import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    t = G.torch()
+    assert t.cuda.is_available(), "no GPU visible"
+    rc = moss.moss_device_check(0)
+    assert rc == moss.MOSS_OK, f"device 0 is not gfx950: {moss.moss_status_string(rc)}"
+    return t
+
+
+# ---- rotary tables ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("n_txt,gh,gw", [(8, 8, 8), (34, 64, 64), (63, 55, 75), (0, 3, 5)])
+def test_rope_build(n_txt, gh, gw):
+    G.say(f"rope_build n_txt={n_txt} grid={gh}x{gw}")
+    rows = n_txt + gh * gw
+    rope = G.empty_f32(2, rows, 64)
+    moss.moss_rope_build(n_txt, gh, gw, 10000.0, rope)
+    G.sync()
+    got = rope.cpu().numpy().astype(np.float64)
+    cos, sin = ob.rope_tables(n_txt, gh, gw, 10000.0, 128)
+    ref = np.stack([ob.round_f32(cos), ob.round_f32(sin)])
+    exact = float(np.mean(got == ref))
+    # both sides evaluate in fp64 and round to fp32; allow one fp32 ulp where libm differs
+    assert np.max(np.abs(got - ref)) <= 2.0 ** -24 * 1.0001, np.max(np.abs(got - ref))
+    assert exact > 0.999, exact
+
+
+# ---- a0 join ------------------------------------------------------------------------------
+
+def test_join_rows_pad_rows_are_zero():
+    geom = synth.smaller(synth.CONFIGS["c0"], batch=3, txt_len=(8, 3, 0))
+    acts = synth.make_activations(geom, 1)
+    txt = acts["txt"].copy()
+    txt[1, 3:] = 0x3F80  # pad rows hold 1.0: must not be read
+    txt[2, :] = 0x4000
+    G.say("join_rows B=3 txt_len=(8,3,0)")
+    out = G.empty_bf16(3, geom.rows, geom.d_model)
+    moss.moss_k_join_rows(3, geom.n_txt, geom.n_img, geom.d_model, G.dev(acts["x"]), G.dev(txt), acts["txt_len"], out)
+    G.sync()
+    ref = ob.join_rows(ob.widen_bf16(acts["x"]), ob.widen_bf16(txt), acts["txt_len"])
+    np.testing.assert_array_equal(G.host_f64(out), ref)
+
+
+# ---- a1 adaLN GEMV ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("batch,d", [(1, 256), (2, 3072), (5, 1024)])
+def test_adaln_gemv(batch, d):
+    G.say(f"adaln_gemv B={batch} D={d}")
+    cond = synth.make_tensor(2, 0, (batch, d))
+    w = synth.make_tensor(2, 1, (6 * d, d), std=0.02)
+    mod = G.empty_f32(batch, 6 * d)
+    ws = G.empty_f32(batch * d)
+    moss.moss_k_adaln_gemv(batch, d, G.dev(cond), G.dev(w), mod, ws)
+    G.sync()
+    ref = ob.adaln_modulation(ob.widen_bf16(cond), ob.widen_bf16(w))
+    got = mod.cpu().numpy().astype(np.float64)
+    # fp32 sums of D terms: error well under 1e-5 of the largest value
+    assert np.max(np.abs(got - ref)) <= 1e-5 * np.max(np.abs(ref))
+    G.assert_parity("mod", got, ref, cos_min=0.9999999)
+
+
+# ---- a2/a8 modulated RMSNorm ------------------------------------------------------------------
+
+@pytest.mark.parametrize("batch,rows,d", [(1, 72, 256), (2, 130, 3072), (1, 33, 8192), (3, 5, 384)])
+def test_mod_rmsnorm(batch, rows, d):
+    G.say(f"mod_rmsnorm B={batch} rows={rows} D={d}")
+    h = synth.make_tensor(3, 0, (batch, rows, d), std=1.5)
+    mod = ob.widen_bf16(synth.make_tensor(3, 1, (batch, 6 * d), std=0.7)).astype(np.float32)
+    out = G.empty_bf16(batch, rows, d)
+    mod_d = G.dev_f32(mod)
+    moss.moss_k_mod_rmsnorm(batch, rows, d, 1e-6, G.dev(h), mod_d[:, 3 * d:], mod_d[:, 4 * d:], 6 * d, out)
+    G.sync()
+    m = mod.astype(np.float64)
+    ref = ob.modulated_rmsnorm(ob.widen_bf16(h), m[:, None, 3 * d:4 * d], m[:, None, 4 * d:5 * d], 1e-6)
+    G.assert_ulps("a", G.host_f64(out), ref, ulps=1.0, abs_floor=1e-5)
+
+
+# ---- GEMM -----------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("m,n,k", [
+    (72, 768, 256),      # the small workload's QKV
+    (300, 256, 512),     # ragged M, one N tile
+    (1058, 384, 256),    # N not a multiple of 256 (128-wide tiles)
+    (4130, 3072, 3072),  # the 4096+34-row out projection
+    (513, 24576, 3072),  # the up projection's width, ragged M
+    (257, 3072, 12288),  # the down projection's depth
+])
+def test_gemm_nt(m, n, k):
+    G.say(f"gemm_nt M={m} N={n} K={k}")
+    a = synth.make_tensor(4, 0, (m, k))
+    w = synth.make_tensor(4, 1, (n, k), std=0.02)
+    c = G.empty_bf16(m, n)
+    moss.moss_k_gemm_nt(m, n, k, G.dev(a), k, G.dev(w), k, c, n)
+    G.sync()
+    rows = np.arange(m) if m * n <= 4_000_000 else np.unique(np.r_[0:64, m - 64:m, np.linspace(0, m - 1, 200).astype(int)])
+    ref = ob.widen_bf16(a[rows]) @ ob.widen_bf16(w).T
+    got = G.host_f64(c)[rows]
+    # one bf16 rounding of an fp32 sum of K terms
+    G.assert_ulps("c", got, ref, ulps=1.0, abs_floor=2e-6 * np.sqrt(k))
+
+
+def test_gemm_strided():
+    """Row strides larger than the logical widths (a column slice of a wider matrix)."""
+    m, n, k = 200, 256, 256
+    a = synth.make_tensor(5, 0, (m, 2 * k))
+    w = synth.make_tensor(5, 1, (n, k + 64), std=0.02)
+    c = G.empty_bf16(m, n + 128)
+    c.zero_()
+    G.say("gemm_nt strided")
+    moss.moss_k_gemm_nt(m, n, k, G.dev(a), 2 * k, G.dev(w), k + 64, c, n + 128)
+    G.sync()
+    ref = ob.widen_bf16(a[:, :k]) @ ob.widen_bf16(w[:, :k]).T
+    got = G.host_f64(c)
+    G.assert_ulps("c", got[:, :n], ref, ulps=1.0, abs_floor=1e-4)
+    assert np.all(got[:, n:] == 0)
+
+
+# ---- a4 q/k norm + rotary + pack --------------------------------------------------------------------
+
+@pytest.mark.parametrize("batch,n_txt,gh,gw,heads", [(1, 8, 8, 8, 2), (2, 34, 8, 12, 3), (1, 63, 11, 15, 2)])
+def test_qk_norm_rope_pack(batch, n_txt, gh, gw, heads):
+    rows = n_txt + gh * gw
+    d = heads * 128
+    G.say(f"qk_norm_rope_pack B={batch} rows={rows} H={heads}")
+    qkv = synth.make_tensor(6, 0, (batch, rows, 3 * d), std=1.3)
+    gq = synth.normal_bf16(6, (0, 50), (128,), 0.02, offset=1.0)
+    gk = synth.normal_bf16(6, (0, 51), (128,), 0.02, offset=1.0)
+    rope = G.empty_f32(2, rows, 64)
+    moss.moss_rope_build(n_txt, gh, gw, 10000.0, rope)
+    rp = moss.moss_packed_rows(rows)
+    q = G.empty_bf16(batch, heads, rp, 128)
+    k = G.empty_bf16(batch, heads, rp, 128)
+    v = G.empty_bf16(batch, heads, rp // 64, 128, 64)
+    for t_ in (q, k, v):
+        t_.fill_(0x7FC0)  # NaN pattern: every element must be written
+    moss.moss_k_qk_norm_rope_pack(batch, rows, heads, 1e-6, G.dev(qkv), G.dev(gq), G.dev(gk), rope, q, k, v)
+    G.sync()
+    cos, sin = ob.rope_tables(n_txt, gh, gw, 10000.0, 128)
+    x = ob.widen_bf16(qkv).reshape(batch, rows, 3, heads, 128).transpose(0, 2, 3, 1, 4)  # [B, 3, H, T, 128]
+    qb, kb = G.host_bits(q), G.host_bits(k)
+    vb, vpad = G.unpack_v(G.host_bits(v), rows)
+    for b in range(batch):
+        rq, rk = ob.qk_norm_rope(x[b, 0], x[b, 1], ob.widen_bf16(gq), ob.widen_bf16(gk), cos, sin, 1e-6)
+        G.assert_ulps(f"q[{b}]", ob.widen_bf16(qb[b, :, :rows]), rq, ulps=1.0, abs_floor=2e-5)
+        G.assert_ulps(f"k[{b}]", ob.widen_bf16(kb[b, :, :rows]), rk, ulps=1.0, abs_floor=2e-5)
+        src_v = qkv.reshape(batch, rows, 3, heads, 128)[b, :, 2].transpose(1, 0, 2)
+        np.testing.assert_array_equal(vb[b], src_v)
+    assert np.all(qb[:, :, rows:] == 0) and np.all(kb[:, :, rows:] == 0) and np.all(vpad == 0)
+
+
+# ---- a5 attention -------------------------------------------------------------------------------------
+
+def _attention_case(batch, heads, rows, n_txt, lens, seed, q_scale=1.0, qkv_bits=None):
+    if qkv_bits is None:
+        q = synth.make_tensor(seed, 0, (batch, heads, rows, 128), std=q_scale)
+        k = synth.make_tensor(seed, 1, (batch, heads, rows, 128))
+        v = synth.make_tensor(seed, 2, (batch, heads, rows, 128), std=1.3)
+    else:
+        q, k, v = qkv_bits
+    rp = moss.moss_packed_rows(rows)
+    o = G.empty_bf16(batch, rows, heads * 128)
+    moss.moss_k_attention(batch, heads, rows, n_txt, lens, G.dev(G.pack_qk(q, rp)), G.dev(G.pack_qk(k, rp)),
+                          G.dev(G.pack_v(v, rp)), o)
+    G.sync()
+    got = G.host_f64(o).reshape(batch, rows, heads, 128).transpose(0, 2, 1, 3)
+    refs = []
+    for b in range(batch):
+        valid = ob.key_mask(n_txt, rows - n_txt, [lens[b] if lens is not None else n_txt])[0]
+        refs.append(ob.attention(ob.widen_bf16(q[b]), ob.widen_bf16(k[b]), ob.widen_bf16(v[b]), valid))
+    return got, np.stack(refs)
+
+
+@pytest.mark.parametrize("batch,heads,rows,n_txt,lens", [
+    (1, 2, 72, 8, None),            # the small workload
+    (2, 2, 4130, 34, (34, 10)),     # guidance pair at 4096+34 rows, 24 pad keys in item 2
+    (1, 2, 4188, 63, None),         # 75x55 grid + 63 text rows: ragged key and query tiles
+    (1, 3, 200, 150, (1,)),         # a whole 64-key tile of padding, one valid text key
+    (1, 1, 1, 1, None),             # a single row
+])
+def test_attention(batch, heads, rows, n_txt, lens):
+    G.say(f"attention B={batch} H={heads} rows={rows} n_txt={n_txt} lens={lens}")
+    got, ref = _attention_case(batch, heads, rows, n_txt, lens, seed=7)
+    G.assert_parity("o", got, ref, cos_min=0.99995, rel_max=1e-2)
+
+
+def test_attention_sharp_logits():
+    """Logits about N(0, 16): exercises the running-max rescale."""
+    G.say("attention sharp logits")
+    got, ref = _attention_case(1, 2, 1000, 10, None, seed=8, q_scale=4.0)
+    G.assert_parity("o", got, ref, cos_min=0.99995, rel_max=1e-2)
+
+
+def test_attention_cancellation():
+    """Equal scores over values of +-2^22 that cancel, plus a small signal.
+
+    After the pages' gate 4 for attention (MOSS-Image encoder page, PR #1512,
+    "Receipt": equal scores over values whose sums reach about 2^22 and
+    cancel).  q = 0 makes every score 0, so every p is exactly 1 and each
+    output is the plain mean of the values.  Keys come in pairs; in each
+    16-key group one pair holds (signal, 0) and the other seven hold
+    (+2^22, -2^22).  Signals are multiples of 4 in [-64, 64], so every
+    partial sum, in any order, is a multiple of 4 below 2^26 and exact in
+    fp32: the output must be the exact mean rounded once to bf16.
+    """
+    rows, heads = 512, 1
+    q = np.zeros((1, heads, rows, 128), dtype=np.uint16)
+    k = synth.make_tensor(9, 1, (1, heads, rows, 128))
+    r = np.arange(rows)[:, None]
+    pair_sig = (r // 2) % 8 == 0
+    sig = np.clip(np.round(ob.widen_bf16(synth.make_tensor(9, 2, (rows, 128), std=30.0)) / 4.0) * 4.0, -64, 64)
+    big = np.where(r % 2 == 0, 1.0, -1.0) * 2.0 ** 22 * np.ones((rows, 128))
+    vals = np.where(pair_sig, np.where(r % 2 == 0, sig, 0.0), big)
+    v = synth.f32_to_bf16_bits(vals.astype(np.float32))[None, None]
+    assert np.array_equal(ob.widen_bf16(v)[0, 0], vals)
+    G.say("attention cancellation")
+    got, ref = _attention_case(1, heads, rows, 0, None, seed=9, qkv_bits=(q, k, v))
+    G.assert_ulps("o", got, ref, ulps=0.5, abs_floor=0.0)
+
+
+# ---- a10 SiLU product, a7/a12 gated add -----------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,f", [(72, 1024), (1033, 12288), (7, 128)])
+def test_silu_mul(rows, f):
+    G.say(f"silu_mul rows={rows} F={f}")
+    u = synth.make_tensor(10, 0, (rows, 2 * f), std=2.0)
+    z = G.empty_bf16(rows, f)
+    moss.moss_k_silu_mul(rows, f, G.dev(u), z)
+    G.sync()
+    uu = ob.widen_bf16(u)
+    ref = ob.silu_gate(uu, f)
+    G.assert_ulps("z", G.host_f64(z), ref, ulps=1.0, abs_floor=1e-6)
+
+
+@pytest.mark.parametrize("batch,rows,d", [(1, 72, 256), (2, 4130, 3072), (3, 9, 384)])
+def test_gated_add(batch, rows, d):
+    G.say(f"gated_add B={batch} rows={rows} D={d}")
+    h = synth.make_tensor(11, 0, (batch, rows, d))
+    y = synth.make_tensor(11, 1, (batch, rows, d), std=0.8)
+    gate = ob.widen_bf16(synth.make_tensor(11, 2, (batch, 6 * d), std=0.7)).astype(np.float32)
+    hd = G.dev(h)
+    gd = G.dev_f32(gate)
+    moss.moss_k_gated_add(batch, rows, d, hd, gd[:, 2 * d:], 6 * d, G.dev(y))
+    G.sync()
+    ref = ob.gated_add(ob.widen_bf16(h), gate.astype(np.float64)[:, None, 2 * d:3 * d], ob.widen_bf16(y))
+    G.assert_ulps("h", G.host_f64(hd), ref, ulps=0.5, abs_floor=1e-6)
