@@ -2,76 +2,113 @@
 // sums and a bf16 result (the MOSS-Image transformer page, TensorFold PR #1528,
 // "What it adds": bf16 GEMMs with fp32 sums).
 //
-// gfx950 design: a workgroup computes a BM x BN tile of c with
-// v_mfma_f32_32x32x16_bf16.  K advances 64 at a time through two LDS stages:
-// while the MFMAs consume one stage, the next k-slab is loaded from global
-// memory into registers and stored into the other stage after the MFMAs, one
-// barrier per slab.  Rows of an LDS slab are 128 bytes (64 bf16 of k); the
-// 16-byte chunk c of row r is stored at chunk c ^ (r & 7), so the 32 rows a
-// wavefront reads for one MFMA operand fall on distinct banks.
+// gfx950 design.  A workgroup of 8 wavefronts computes a 256 x BN tile of c
+// with v_mfma_f32_32x32x16_bf16; each wavefront owns a (256/WM) x (BN/WN)
+// sub-tile whose fp32 accumulators stay in registers for the whole K loop.
 //
-// The MFMA's first operand is the weight tile and its second the activation
-// tile, so each lane's 16 accumulators hold four runs of four consecutive
-// output columns of one output row: the result leaves in 8-byte stores.
-// There is no split-K and no atomic, so results are identical call to call.
+//  * K advances 32 at a time through a ring of four LDS stages.  Each slab is
+//    fetched straight into LDS with global_load_lds_dwordx4 three slabs ahead
+//    of its use, so no register staging or LDS store instruction is needed.
+//  * The MFMA operands of a slab are read from LDS into registers one k-step
+//    ahead, across the slab boundary: when a wavefront reaches the barrier
+//    that ends slab kt, the fragments of slab kt+1 are already in flight, and
+//    slab kt+2 must be resident.  The barrier is a plain s_barrier after an
+//    explicit vmcnt wait that leaves the newest slab's loads outstanding.
+//  * A slab row is 64 bytes (32 bf16 of k).  The 16-byte chunk c of row r is
+//    stored at c ^ ((r >> 2) & 3), so the 16 rows a 16-lane group reads for
+//    one operand fragment land in 16 distinct 16-byte slots of the LDS banks.
+//  * Tiles are numbered M-fastest and grouped per XCD: workgroup ids are
+//    dealt round-robin over the 8 XCDs, so consecutive ids are remapped to
+//    give each XCD a contiguous run of tiles that share weight slabs in its L2.
+//  * The weight tile is the MFMA's first operand and the activation tile the
+//    second, so a lane's accumulators hold runs of four consecutive output
+//    columns of one row and leave in 8-byte stores.
+// There is no split-K and no atomic: results are identical call to call.
 #include "common.h"
 #include "launch.h"
 
 namespace {
 
-constexpr int BK = 64;
+constexpr int KB = 32;      // k per slab
+constexpr int STAGES = 4;   // LDS ring depth
+
+// Workgroup id -> (tile_m, tile_n), M fastest, a contiguous run of tiles per XCD.
+__device__ __forceinline__ void tile_of(int id, int nblk, int mt, int& tm, int& tn) {
+  const int per = nblk / 8, rem = nblk % 8;
+  const int x = id % 8, l = id / 8;
+  const int logical = (x < rem) ? x * (per + 1) + l : rem * (per + 1) + (x - rem) * per + l;
+  tm = logical % mt;
+  tn = logical / mt;
+}
 
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __restrict__ a, int lda,
                                                              const uint16_t* __restrict__ w, int ldw,
-                                                             uint16_t* __restrict__ c, int ldc, int m, int k) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int TM = BM / WM, TN = BN / WN;  // wavefront tile (rows of c, columns of c)
+                                                             uint16_t* __restrict__ c, int ldc, int m, int n,
+                                                             int k) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int ACH = BM * BK / 8, BCH = BN * BK / 8;  // 16-byte chunks per slab
-  constexpr int LA = ACH / NT, LB = BCH / NT;
-  static_assert(LA * NT == ACH && LB * NT == BCH, "tile / thread mismatch");
+  constexpr int AB = BM * KB * 2, BB = BN * KB * 2;          // bytes per slab
+  constexpr int LA = AB / 1024 / NW, LB = BB / 1024 / NW;    // 1 KiB load instructions per wavefront
+  constexpr int PER = LA + LB;
+  static_assert(LA * NW * 1024 == AB && LB * NW * 1024 == BB, "slab / wavefront mismatch");
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * (AB + BB)];
 
-  __shared__ u32x4 sa[2][ACH];
-  __shared__ u32x4 sb[2][BCH];
-
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int mt = (m + BM - 1) / BM;
+  int tm, tn;
+  tile_of(blockIdx.x, mt * (n / BN), mt, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
   const int wm = wave / WN, wn = wave % WN;
 
-  // global -> register loads of one k-slab (rows past m are clamped; their results are never stored)
-  const uint16_t* pa[LA];
-  const uint16_t* pb[LB];
+  // Load instruction i of wavefront `wave` fills the 1 KiB at (wave + NW*i) of a slab: rows
+  // 16*(wave + NW*i) + lane/4, stored slot lane%4, which holds chunk (lane%4) ^ ((row >> 2) & 3).
+  // Rows past m are clamped to m - 1; their results are never stored.
+  const uint16_t* ga[LA];
+  const uint16_t* gb[LB];
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
-    const int id = tid + NT * i, r = id >> 3, ch = id & 7;
-    const int row = min(m0 + r, m - 1);
-    pa[i] = a + (size_t)row * lda + ch * 8;
+    const int r = (wave + NW * i) * 16 + (lane >> 2);
+    ga[i] = a + (size_t)min(m0 + r, m - 1) * lda + ((lane & 3) ^ ((r >> 2) & 3)) * 8;
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
-    const int id = tid + NT * i, r = id >> 3, ch = id & 7;
-    pb[i] = w + (size_t)(n0 + r) * ldw + ch * 8;
+    const int r = (wave + NW * i) * 16 + (lane >> 2);
+    gb[i] = w + (size_t)(n0 + r) * ldw + ((lane & 3) ^ ((r >> 2) & 3)) * 8;
   }
-  u32x4 ra[LA], rb[LB];
-  auto gload = [&](int k0) {
+  auto issue = [&](int slab) {
+    MOSS_LDS char* base = (MOSS_LDS char*)smem + (slab % STAGES) * (AB + BB);
 #pragma unroll
-    for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + k0);
+    for (int i = 0; i < LA; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(ga[i] + slab * KB),
+                                       (MOSS_LDS void*)(base + 1024 * (wave + NW * i)), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < LB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + k0);
+    for (int i = 0; i < LB; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(gb[i] + slab * KB),
+                                       (MOSS_LDS void*)(base + AB + 1024 * (wave + NW * i)), 16, 0, 0);
   };
-  auto sstore = [&](int buf) {
+  // byte offsets of this lane's fragments within a stage, for the two k16 steps of a slab
+  int offa[2][FM], offb[2][FN];
 #pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int id = tid + NT * i, r = id >> 3, ch = id & 7;
-      sa[buf][r * 8 + (ch ^ (r & 7))] = ra[i];
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int r = wm * TM + j * 32 + l32;
+      offa[s][j] = r * 64 + ((2 * s + hh) ^ ((r >> 2) & 3)) * 16;
     }
 #pragma unroll
-    for (int i = 0; i < LB; ++i) {
-      const int id = tid + NT * i, r = id >> 3, ch = id & 7;
-      sb[buf][r * 8 + (ch ^ (r & 7))] = rb[i];
+    for (int i = 0; i < FN; ++i) {
+      const int r = wn * TN + i * 32 + l32;
+      offb[s][i] = AB + r * 64 + ((2 * s + hh) ^ ((r >> 2) & 3)) * 16;
     }
+  }
+  auto ldfrag = [&](int slab, int s, bf16x8* fa, bf16x8* fw) {
+    const char* base = smem + (slab % STAGES) * (AB + BB);
+#pragma unroll
+    for (int j = 0; j < FM; ++j) fa[j] = *reinterpret_cast<const bf16x8*>(base + offa[s][j]);
+#pragma unroll
+    for (int i = 0; i < FN; ++i) fw[i] = *reinterpret_cast<const bf16x8*>(base + offb[s][i]);
   };
 
   f32x16 acc[FN][FM];
@@ -82,33 +119,33 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int nk = k / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  const int nk = k / KB;
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < nk) issue(p);
+  // slabs 0 and 1 resident before the loop (iteration 0 prefetches slab 1)
+  if (nk >= 3) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(PER) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+
+  bf16x8 fa0[FM], fw0[FN], fa1[FM], fw1[FN];
+  ldfrag(0, 0, fa0, fw0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+    // stage (kt+3)%4 held slab kt-1, whose last reads finished before the previous barrier
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+    ldfrag(kt, 1, fa1, fw1);
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      bf16x8 fw[FN], fa[FM];
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        const int r = wn * TN + i * 32 + l32;
-        fw[i] = __builtin_bit_cast(bf16x8, sb[buf][r * 8 + ((2 * s + hh) ^ (r & 7))]);
-      }
+      for (int j = 0; j < FM; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw0[i], fa0[j], acc[i][j], 0, 0, 0);
+    // slab kt+1 is resident; the last iteration re-reads its own stage so the wait counts stay exact
+    ldfrag(kt + 1 < nk ? kt + 1 : kt, 0, fa0, fw0);
 #pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const int r = wm * TM + j * 32 + l32;
-        fa[j] = __builtin_bit_cast(bf16x8, sa[buf][r * 8 + ((2 * s + hh) ^ (r & 7))]);
-      }
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fa[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
+      for (int j = 0; j < FM; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw1[i], fa1[j], acc[i][j], 0, 0, 0);
+    // slab kt+2 resident for the next iteration (only slab kt+3 may stay in flight)
+    if (kt + STAGES - 1 < nk) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(PER) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
   // acc[i][j] is a 32 x 32 tile of c^T: lane holds row m = l32 of c and
@@ -136,14 +173,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
 
 hipError_t launch_gemm_nt(int m, int n, int k, const uint16_t* a, int lda, const uint16_t* w, int ldw,
                           uint16_t* c, int ldc, hipStream_t st) {
+  const int mt = (m + 255) / 256;
   if (n % 256 == 0) {
-    constexpr int BM = 256, BN = 256;
-    hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, 2, 4>), dim3(n / BN, (m + BM - 1) / BM), dim3(512), 0, st, a, lda,
-                       w, ldw, c, ldc, m, k);
+    hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4>), dim3(mt * (n / 256)), dim3(512), 0, st, a, lda, w, ldw, c,
+                       ldc, m, n, k);
   } else {
-    constexpr int BM = 256, BN = 128;
-    hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, 4, 2>), dim3(n / BN, (m + BM - 1) / BM), dim3(512), 0, st, a, lda,
-                       w, ldw, c, ldc, m, k);
+    hipLaunchKernelGGL((gemm_nt_kernel<256, 128, 4, 2>), dim3(mt * (n / 128)), dim3(512), 0, st, a, lda, w, ldw, c,
+                       ldc, m, n, k);
   }
   return hipGetLastError();
 }
