@@ -5,20 +5,31 @@
 //
 // gfx950 design.  A workgroup owns 128 queries of one (item, head); each of
 // its four wavefronts owns 32 queries and keeps them in registers as MFMA
-// operands for the whole key loop.  Keys advance 64 at a time through two LDS
-// stages (K rows, and V transposed as packed by the q/k kernel).
+// operands for the whole key loop.  Two workgroups share a CU (2 wavefronts
+// per SIMD), so one wavefront's softmax overlaps the other's MFMAs.
 //
-// Per key tile a wavefront computes S^T = K Q^T (keys x queries) with
-// v_mfma_f32_32x32x16_bf16, so a lane holds 32 of the 64 scores of ONE query
-// (lane l and lane l ^ 32 share a query and split its keys).  The running
-// max and sum need one exchange between the two half-waves.  The
-// probabilities, rounded to bf16, are already laid out as the second operand
-// of O^T += V^T P^T: the key order inside each 16-key group of the packed V
-// matches the order in which a lane holds its scores.  O^T stays in 64
-// accumulators per lane; no probability goes through LDS.
-//
+//  * Keys advance 64 at a time through two LDS stages (K rows, and V
+//    transposed as the q/k kernel packs it), each filled straight from
+//    global memory with global_load_lds_dwordx4 one tile ahead.  The K chunk
+//    c of key row r is stored at c ^ (r & 15) (256-byte rows) and the V
+//    chunk c of dim row d at c ^ ((d >> 1) & 7) (128-byte rows), so the 16
+//    rows a 16-lane group reads fall in distinct 16-byte bank slots.
+//  * Per key tile a wavefront computes S^T = K Q^T (keys x queries) with
+//    v_mfma_f32_32x32x16_bf16, so lane l holds 32 of the 64 scores of ONE
+//    query and lane l ^ 32 the other 32; the max and the sum need one
+//    v_permlane32_swap each.
+//  * Scores are scaled into log2 units inside the exp2 argument (one FMA per
+//    score) and exponentiated with v_exp_f32 directly (results below 2^-126
+//    of the row max flush to zero, which no bf16 probability could hold).  The running max used for the exponentials only moves when a
+//    row's max grows by more than 8 (in log2 units) anywhere in the
+//    wavefront; until then probabilities may reach 2^8, which fp32 sums and
+//    bf16 products hold exactly as well, and O and the sum need no rescale.
+//  * The probabilities, rounded to bf16, are already laid out as the second
+//    operand of O^T += V^T P^T (the packed V stores the keys of each 16-key
+//    group in the order a lane holds its scores).  O^T stays in 64
+//    accumulators per lane; no probability goes through LDS.
 // Keys that are text padding (txt_len <= key < n_txt) or past the last row
-// get -inf before the max; a tile with no valid key leaves the state as is.
+// get -inf; a tile with no valid key leaves the state as it is.
 #include <math.h>
 
 #include "common.h"
@@ -29,18 +40,28 @@ namespace {
 constexpr int BQ = 128;  // queries per workgroup
 constexpr int BKV = 64;  // keys per tile
 constexpr int kThreads = 256;
+constexpr int kStage = 32768;  // K tile (16 KiB) then V^T tile (16 KiB)
+constexpr float kLazy = 8.0f;  // log2-unit growth of a row max that forces a rescale
 
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const uint16_t* __restrict__ qp,
-                                                            const uint16_t* __restrict__ kp,
-                                                            const uint16_t* __restrict__ vp,
-                                                            uint16_t* __restrict__ o, int rows, int rows_pad,
-                                                            int n_heads, int n_txt, ItemLens lens,
-                                                            float scale_log2) {
-  __shared__ u32x4 sk[2][BKV * 16];  // 64 keys x 16 chunks (256 B per key)
-  __shared__ u32x4 sv[2][128 * 8];   // 128 dims x 8 chunks (64 keys per dim)
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const uint16_t* __restrict__ qp,
+                                                               const uint16_t* __restrict__ kp,
+                                                               const uint16_t* __restrict__ vp,
+                                                               uint16_t* __restrict__ o, int rows, int rows_pad,
+                                                               int n_heads, int n_txt, ItemLens lens,
+                                                               float scale_log2) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
 
   const int qt = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
   const size_t bh = (size_t)b * n_heads + head;
   const uint16_t* qb = qp + bh * rows_pad * 128;
   const uint16_t* kb = kp + bh * rows_pad * 128;
@@ -56,115 +77,126 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const uint16_t* __re
     for (int s = 0; s < 8; ++s) qf[s] = __builtin_bit_cast(bf16x8, src[2 * s + hh]);
   }
 
+  // direct-to-LDS load sources: instruction i of this wavefront fills 1 KiB block (wave + 4i)
+  // of the K tile (4 key rows of 256 B) and of the V^T tile (8 dim rows of 128 B)
+  int koff[4], voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int blk = wave + 4 * i;
+    const int key = blk * 4 + (lane >> 4);
+    koff[i] = key * 128 + (((lane & 15) ^ (key & 15)) * 8);
+    const int dim = blk * 8 + (lane >> 3);
+    voff[i] = dim * 64 + (((lane & 7) ^ ((dim >> 1) & 7)) * 8);
+  }
+  auto issue = [&](int kt) {
+    MOSS_LDS char* base = (MOSS_LDS char*)smem + (kt & 1) * kStage;
+    const uint16_t* ks = kb + (size_t)kt * BKV * 128;
+    const uint16_t* vs = vb + (size_t)kt * BKV * 128;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_global_load_lds((const void*)(ks + koff[i]), (MOSS_LDS void*)(base + 1024 * (wave + 4 * i)),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vs + voff[i]),
+                                       (MOSS_LDS void*)(base + 16384 + 1024 * (wave + 4 * i)), 16, 0, 0);
+    }
+  };
+  // this lane's fragment offsets within a stage
+  int kfo[2][8], vfo[4][4];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int key = h2 * 32 + l32;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kfo[h2][s] = key * 256 + (((2 * s + hh) ^ (key & 15)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int dim = i * 32 + l32;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) vfo[i][s] = 16384 + dim * 128 + (((2 * s + hh) ^ ((dim >> 1) & 7)) * 16);
+  }
+
   f32x16 acc_o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc_o[i][e] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_use = -INFINITY;  // max (log2 units, scaled) the exponentials are taken against
+  float l_run = 0.0f;
 
   const int n_tiles = (rows + BKV - 1) / BKV;
-  u32x4 rk[4], rv[4];
-  auto gload = [&](int kt) {
-    const u32x4* ks = reinterpret_cast<const u32x4*>(kb + (size_t)kt * BKV * 128);
-    const u32x4* vs = reinterpret_cast<const u32x4*>(vb + (size_t)kt * BKV * 128);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rk[i] = ks[tid + kThreads * i];
-      rv[i] = vs[tid + kThreads * i];
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + kThreads * i;
-      const int key = id >> 4, ck = id & 15;
-      sk[buf][key * 16 + (ck ^ (key & 7))] = rk[i];
-      const int dim = id >> 3, cv = id & 7;
-      sv[buf][dim * 8 + (cv ^ (dim & 7))] = rv[i];
-    }
-  };
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  issue(0);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   for (int kt = 0; kt < n_tiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_tiles) gload(kt + 1);
+    // stage (kt+1)&1 held tile kt-1, whose reads finished before the previous barrier
+    if (kt + 1 < n_tiles) issue(kt + 1);
+    const char* st = smem + (kt & 1) * kStage;
 
-    // S^T for two 32-key halves of the tile
     f32x16 sacc[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[h2][e] = 0.0f;
-      const int key = h2 * 32 + l32;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, sk[buf][key * 16 + ((2 * s + hh) ^ (key & 7))]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(st + kfo[h2][s]);
         sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[h2], 0, 0, 0);
       }
     }
 
-    // scores in log2 units; lane holds keys 32*h2 + 8*q + 4*hh + e at sacc[h2][4q + e]
+    // lane holds keys 32*h2 + 8*q + 4*hh + e at sacc[h2][4q + e]
     const int key0 = kt * BKV;
-    const bool need_mask = (key0 + BKV > rows) || (key0 < n_txt && key0 + BKV > valid_txt);
-    float mloc = -INFINITY;
+    if ((key0 + BKV > rows) || (key0 < n_txt && key0 + BKV > valid_txt)) {
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float sv2 = sacc[h2][e] * scale_log2;
-        if (need_mask) {
+        for (int e = 0; e < 16; ++e) {
           const int key = key0 + h2 * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
           const bool bad = (key >= rows) || (key >= valid_txt && key < n_txt);
-          sv2 = bad ? -INFINITY : sv2;
+          sacc[h2][e] = bad ? -INFINITY : sacc[h2][e];
         }
-        sacc[h2][e] = sv2;
-        mloc = fmaxf(mloc, sv2);
-      }
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(m_run, mloc);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float corr = exp2f(m_run - m_use);
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[h2][e]);
+    mloc = pair_max(mloc) * scale_log2;
+    // move the reference max (for every row of the wavefront at once) only when some row grew a lot
+    if (__builtin_amdgcn_ballot_w64(mloc > m_use + kLazy) != 0ull) {
+      const float m_new = fmaxf(m_use, mloc);
+      const float corr = __builtin_amdgcn_exp2f(m_use - m_new);  // 0 on the first valid tile
+      l_run *= corr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc_o[i][e] *= corr;
+      m_use = m_new;
+    }
+    const float moff = (m_use == -INFINITY) ? 0.0f : m_use;
     float lsum = 0.0f;
     bf16x8 pf[4];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        float p[8];
+      for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          p[t] = exp2f(sacc[h2][8 * half + t] - m_use);
-          lsum += p[t];
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[h2][8 * half + t], scale_log2, -moff));
+          lsum += p;
+          pf[2 * h2 + half][t] = (__bf16)p;
         }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) pf[2 * h2 + half][t] = (__bf16)p[t];
-      }
-    }
-    lsum += __shfl_xor(lsum, 32, 64);
-    l_run = l_run * corr + lsum;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc_o[i][e] *= corr;
+    l_run += pair_sum(lsum);
 
     // O^T += V^T P^T over four 16-key steps
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int dim = i * 32 + l32;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, sv[buf][dim * 8 + ((2 * s + hh) ^ (dim & 7))]);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(st + vfo[i][s]);
         acc_o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], acc_o[i], 0, 0, 0);
       }
-    }
 
-    if (kt + 1 < n_tiles) sstore(buf ^ 1);
-    __syncthreads();
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   }
 
   // acc_o[i][4q + e] = O^T[dim = 32 i + 8 q + 4 hh + e][query l32]
