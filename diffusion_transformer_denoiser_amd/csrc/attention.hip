@@ -20,10 +20,11 @@
 //    v_permlane32_swap each.
 //  * Scores are scaled into log2 units inside the exp2 argument (one FMA per
 //    score) and exponentiated with v_exp_f32 directly (results below 2^-126
-//    of the row max flush to zero, which no bf16 probability could hold).  The running max used for the exponentials only moves when a
-//    row's max grows by more than 8 (in log2 units) anywhere in the
-//    wavefront; until then probabilities may reach 2^8, which fp32 sums and
-//    bf16 products hold exactly as well, and O and the sum need no rescale.
+//    of the row max flush to zero, which no bf16 probability could hold).
+//    The running max used for the exponentials only moves when a row's max
+//    grows by more than 8 (in log2 units) anywhere in the wavefront; until
+//    then probabilities may reach 2^8, which fp32 sums and bf16 products hold
+//    exactly as well, and O and the sum need no rescale.
 //  * The probabilities, rounded to bf16, are already laid out as the second
 //    operand of O^T += V^T P^T (the packed V stores the keys of each 16-key
 //    group in the order a lane holds its scores).  O^T stays in 64

@@ -12,10 +12,10 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// ---- a0: h0 = [txt; x], pad text rows read as zero -------------------------
+// ---- a0: h0 = [txt; x] into the fp32 residual stream, pad text rows zero ----
 __global__ __launch_bounds__(kThreads) void join_rows_kernel(const u32x4* __restrict__ x,
                                                              const u32x4* __restrict__ txt, ItemLens lens,
-                                                             u32x4* __restrict__ out, int n_txt, int n_img,
+                                                             f32x4* __restrict__ out, int n_txt, int n_img,
                                                              int chunks_per_row, long total) {
   const int rows = n_txt + n_img;
   for (long i = (long)blockIdx.x * kThreads + threadIdx.x; i < total; i += (long)gridDim.x * kThreads) {
@@ -29,7 +29,10 @@ __global__ __launch_bounds__(kThreads) void join_rows_kernel(const u32x4* __rest
     } else {
       v = x[((long)b * n_img + (r - n_txt)) * chunks_per_row + c];
     }
-    out[i] = v;
+    float f[8];
+    unpack8(v, f);
+    out[2 * i] = f32x4{f[0], f[1], f[2], f[3]};
+    out[2 * i + 1] = f32x4{f[4], f[5], f[6], f[7]};
   }
 }
 
@@ -75,12 +78,11 @@ __global__ __launch_bounds__(kThreads) void adaln_gemv_kernel(const float* __res
   }
 }
 
-// ---- a2/a8: modulated RMSNorm, one wavefront per row ------------------------
-// Row values stay in registers between the mean-square pass and the scaling
-// pass (d_model <= 8192 means at most 16 chunks per lane).
-constexpr int kMaxChunksPerLane = MOSS_MAX_DMODEL / 8 / 64;
-
-__global__ __launch_bounds__(kThreads) void mod_rmsnorm_kernel(const uint16_t* __restrict__ h,
+// ---- a2/a8: modulated RMSNorm of the fp32 residual, one wavefront per row ----
+// The row stays in registers between the mean-square pass and the scaling
+// pass: CPL chunks of eight values per lane (CPL * 512 >= d_model).
+template <int CPL>
+__global__ __launch_bounds__(kThreads) void mod_rmsnorm_kernel(const float* __restrict__ h,
                                                                const float* __restrict__ shift,
                                                                const float* __restrict__ scale,
                                                                int mod_stride, uint16_t* __restrict__ out,
@@ -91,18 +93,17 @@ __global__ __launch_bounds__(kThreads) void mod_rmsnorm_kernel(const uint16_t* _
   if (row >= total_rows) return;
   const int b = row / rows_per_item;
   const int nch = d >> 3;
-  const u32x4* src = reinterpret_cast<const u32x4*>(h + (size_t)row * d);
-  u32x4 v[kMaxChunksPerLane];
+  const f32x4* src = reinterpret_cast<const f32x4*>(h + (size_t)row * d);
+  f32x4 v[CPL][2];
   float ss = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kMaxChunksPerLane; ++i) {
+  for (int i = 0; i < CPL; ++i) {
     const int c = lane + 64 * i;
     if (c < nch) {
-      v[i] = src[c];
-      float f[8];
-      unpack8(v[i], f);
+      v[i][0] = src[2 * c];
+      v[i][1] = src[2 * c + 1];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ss += f[j] * f[j];
+      for (int j = 0; j < 4; ++j) ss += v[i][0][j] * v[i][0][j] + v[i][1][j] * v[i][1][j];
     }
   }
   ss = wave_sum(ss);
@@ -111,11 +112,9 @@ __global__ __launch_bounds__(kThreads) void mod_rmsnorm_kernel(const uint16_t* _
   const float* sc = scale + (size_t)b * mod_stride;
   u32x4* dst = reinterpret_cast<u32x4*>(out + (size_t)row * d);
 #pragma unroll
-  for (int i = 0; i < kMaxChunksPerLane; ++i) {
+  for (int i = 0; i < CPL; ++i) {
     const int c = lane + 64 * i;
     if (c < nch) {
-      float f[8];
-      unpack8(v[i], f);
       const f32x4 sh0 = reinterpret_cast<const f32x4*>(sh + 8 * c)[0];
       const f32x4 sh1 = reinterpret_cast<const f32x4*>(sh + 8 * c)[1];
       const f32x4 sc0 = reinterpret_cast<const f32x4*>(sc + 8 * c)[0];
@@ -123,33 +122,43 @@ __global__ __launch_bounds__(kThreads) void mod_rmsnorm_kernel(const uint16_t* _
       float o[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        o[j] = (f[j] * r) * (1.0f + sc0[j]) + sh0[j];
-        o[4 + j] = (f[4 + j] * r) * (1.0f + sc1[j]) + sh1[j];
+        o[j] = (v[i][0][j] * r) * (1.0f + sc0[j]) + sh0[j];
+        o[4 + j] = (v[i][1][j] * r) * (1.0f + sc1[j]) + sh1[j];
       }
       dst[c] = pack8(o);
     }
   }
 }
 
-// ---- a7/a12: h += gate * y, in place ----------------------------------------
-__global__ __launch_bounds__(kThreads) void gated_add_kernel(u32x4* __restrict__ h, const float* __restrict__ gate,
+// ---- a7/a12: h + gate * y on the fp32 residual ------------------------------------
+// In place (out16 == nullptr), or, for the last add of a call, into the bf16
+// output instead.
+__global__ __launch_bounds__(kThreads) void gated_add_kernel(f32x4* __restrict__ h, const float* __restrict__ gate,
                                                              int gate_stride, const u32x4* __restrict__ y,
-                                                             int chunks_per_row, int rows_per_item, long total) {
+                                                             u32x4* __restrict__ out16, int chunks_per_row,
+                                                             int rows_per_item, long total) {
   for (long i = (long)blockIdx.x * kThreads + threadIdx.x; i < total; i += (long)gridDim.x * kThreads) {
     const long row = i / chunks_per_row;
     const int c = (int)(i - row * chunks_per_row);
     const int b = (int)(row / rows_per_item);
     const f32x4* g = reinterpret_cast<const f32x4*>(gate + (size_t)b * gate_stride + 8 * c);
     const f32x4 g0 = g[0], g1 = g[1];
-    float hv[8], yv[8], o[8];
-    unpack8(h[i], hv);
+    const f32x4 h0 = h[2 * i], h1 = h[2 * i + 1];
+    float yv[8];
     unpack8(y[i], yv);
+    f32x4 o0, o1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      o[j] = hv[j] + g0[j] * yv[j];
-      o[4 + j] = hv[4 + j] + g1[j] * yv[4 + j];
+      o0[j] = h0[j] + g0[j] * yv[j];
+      o1[j] = h1[j] + g1[j] * yv[4 + j];
     }
-    h[i] = pack8(o);
+    if (out16) {
+      const float o[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
+      out16[i] = pack8(o);
+    } else {
+      h[2 * i] = o0;
+      h[2 * i + 1] = o1;
+    }
   }
 }
 
@@ -195,12 +204,12 @@ int grid_for(long work, int per_block) {
 
 }  // namespace
 
-hipError_t launch_join_rows(const uint16_t* x, const uint16_t* txt, const ItemLens& lens, uint16_t* out,
-                            int batch, int n_txt, int n_img, int d, hipStream_t st) {
+hipError_t launch_join_rows(const uint16_t* x, const uint16_t* txt, const ItemLens& lens, float* out, int batch,
+                            int n_txt, int n_img, int d, hipStream_t st) {
   const long total = (long)batch * (n_txt + n_img) * (d / 8);
   hipLaunchKernelGGL(join_rows_kernel, dim3(grid_for(total, kThreads)), dim3(kThreads), 0, st,
                      reinterpret_cast<const u32x4*>(x), reinterpret_cast<const u32x4*>(txt), lens,
-                     reinterpret_cast<u32x4*>(out), n_txt, n_img, d / 8, total);
+                     reinterpret_cast<f32x4*>(out), n_txt, n_img, d / 8, total);
   return hipGetLastError();
 }
 
@@ -217,20 +226,29 @@ hipError_t launch_adaln_gemv(const float* s, const uint16_t* w_mod, float* mod, 
   return hipGetLastError();
 }
 
-hipError_t launch_mod_rmsnorm(const uint16_t* h, const float* shift, const float* scale, int mod_stride,
+hipError_t launch_mod_rmsnorm(const float* h, const float* shift, const float* scale, int mod_stride,
                               uint16_t* out, int batch, int rows, int d, float eps, hipStream_t st) {
   const int total = batch * rows;
-  hipLaunchKernelGGL(mod_rmsnorm_kernel, dim3((total + 3) / 4), dim3(kThreads), 0, st, h, shift, scale,
-                     mod_stride, out, total, rows, d, eps);
+  const int cpl = (d / 8 + 63) / 64;
+  const dim3 grid((total + 3) / 4), block(kThreads);
+  if (cpl <= 2)
+    hipLaunchKernelGGL(mod_rmsnorm_kernel<2>, grid, block, 0, st, h, shift, scale, mod_stride, out, total, rows, d, eps);
+  else if (cpl <= 4)
+    hipLaunchKernelGGL(mod_rmsnorm_kernel<4>, grid, block, 0, st, h, shift, scale, mod_stride, out, total, rows, d, eps);
+  else if (cpl <= 8)
+    hipLaunchKernelGGL(mod_rmsnorm_kernel<8>, grid, block, 0, st, h, shift, scale, mod_stride, out, total, rows, d, eps);
+  else
+    hipLaunchKernelGGL(mod_rmsnorm_kernel<16>, grid, block, 0, st, h, shift, scale, mod_stride, out, total, rows, d,
+                       eps);
   return hipGetLastError();
 }
 
-hipError_t launch_gated_add(uint16_t* h, const float* gate, int gate_stride, const uint16_t* y, int batch,
-                            int rows, int d, hipStream_t st) {
+hipError_t launch_gated_add(float* h, const float* gate, int gate_stride, const uint16_t* y, uint16_t* out16,
+                            int batch, int rows, int d, hipStream_t st) {
   const long total = (long)batch * rows * (d / 8);
   hipLaunchKernelGGL(gated_add_kernel, dim3(grid_for(total, kThreads)), dim3(kThreads), 0, st,
-                     reinterpret_cast<u32x4*>(h), gate, gate_stride, reinterpret_cast<const u32x4*>(y), d / 8,
-                     rows, total);
+                     reinterpret_cast<f32x4*>(h), gate, gate_stride, reinterpret_cast<const u32x4*>(y),
+                     reinterpret_cast<u32x4*>(out16), d / 8, rows, total);
   return hipGetLastError();
 }
 

@@ -7,14 +7,15 @@
 
 struct ItemLens;
 
-hipError_t launch_join_rows(const uint16_t* x, const uint16_t* txt, const ItemLens& lens, uint16_t* out,
-                            int batch, int n_txt, int n_img, int d, hipStream_t st);
+hipError_t launch_join_rows(const uint16_t* x, const uint16_t* txt, const ItemLens& lens, float* out, int batch,
+                            int n_txt, int n_img, int d, hipStream_t st);
 hipError_t launch_silu_cond(const uint16_t* cond, float* s, int batch, int d, hipStream_t st);
 hipError_t launch_adaln_gemv(const float* s, const uint16_t* w_mod, float* mod, int batch, int d, hipStream_t st);
-hipError_t launch_mod_rmsnorm(const uint16_t* h, const float* shift, const float* scale, int mod_stride,
+hipError_t launch_mod_rmsnorm(const float* h, const float* shift, const float* scale, int mod_stride,
                               uint16_t* out, int batch, int rows, int d, float eps, hipStream_t st);
-hipError_t launch_gated_add(uint16_t* h, const float* gate, int gate_stride, const uint16_t* y, int batch,
-                            int rows, int d, hipStream_t st);
+// h (fp32) + gate * y: in place when out16 is null, else into out16 (bf16) with h unchanged.
+hipError_t launch_gated_add(float* h, const float* gate, int gate_stride, const uint16_t* y, uint16_t* out16,
+                            int batch, int rows, int d, hipStream_t st);
 hipError_t launch_silu_mul(const uint16_t* u, uint16_t* z, int rows, int f, hipStream_t st);
 hipError_t launch_rope_build(int n_txt, int grid_h, int grid_w, float theta, float* rope, hipStream_t st);
 

@@ -59,10 +59,12 @@ bool lens_ok(const moss_dims* d, const int32_t* txt_len, ItemLens* out) {
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t s_cond, mod, a, y, qkv, qp, kp, vp, u, z, total;
+  size_t s_cond, mod, h, a, y, qkv, qp, kp, vp, u, z, total;
 };
 
-// Offsets (bytes) into the workspace.  a holds the first norm's output, then
+// Offsets (bytes) into the workspace.  h is the fp32 residual stream (the
+// running sum of the gated adds, rounded to bf16 only when `out` is written).
+// a holds the first norm's output, then
 // the attention output, then the second norm's output; y holds each
 // projection output that is added to the residual; the union region holds the
 // qkv rows and packed q/k/v during attention, and the MLP activations after.
@@ -78,6 +80,7 @@ Layout plan(const moss_dims* d) {
   };
   L.s_cond = take(4 * B * D);
   L.mod = take(4 * B * 6 * D);
+  L.h = take(4 * R * D);
   L.a = take(2 * R * D);
   L.y = take(2 * R * D);
   const size_t base = off;
@@ -169,7 +172,9 @@ struct Ctx {
   hipStream_t st;
 };
 
-int run_block(const Ctx& c, const moss_block_weights* w, const float* rope, uint16_t* h) {
+// One block on the fp32 residual h; when out16 is not null the block's last
+// gated add writes the bf16 result there instead of updating h.
+int run_block(const Ctx& c, const moss_block_weights* w, const float* rope, float* h, uint16_t* out16) {
   const moss_dims* d = c.d;
   const int B = d->batch, T = d->n_txt + d->n_img, D = d->d_model, F = d->mlp_inner, H = d->n_heads;
   const int R = B * T;
@@ -212,7 +217,7 @@ int run_block(const Ctx& c, const moss_block_weights* w, const float* rope, uint
   }
   {
     StepTimer t(MOSS_STEP_GATE1, st);
-    MOSS_TRY(launch_gated_add(h, mod + 2 * D, ms, y, B, T, D, st), "gated_add");
+    MOSS_TRY(launch_gated_add(h, mod + 2 * D, ms, y, nullptr, B, T, D, st), "gated_add");
   }
   {
     StepTimer t(MOSS_STEP_NORM2, st);
@@ -232,7 +237,7 @@ int run_block(const Ctx& c, const moss_block_weights* w, const float* rope, uint
   }
   {
     StepTimer t(MOSS_STEP_GATE2, st);
-    MOSS_TRY(launch_gated_add(h, mod + 5 * D, ms, y, B, T, D, st), "gated_add");
+    MOSS_TRY(launch_gated_add(h, mod + 5 * D, ms, y, out16, B, T, D, st), "gated_add");
   }
   return MOSS_OK;
 }
@@ -287,14 +292,15 @@ int forward(const moss_dims* d, int n_blocks, const uint16_t* x, const uint16_t*
   rc = check_current_device();
   if (rc != MOSS_OK) return rc;
   c.st = st;
+  float* h = reinterpret_cast<float*>(c.ws + c.L.h);
   {
     StepTimer t(MOSS_STEP_JOIN, st);
-    MOSS_TRY(launch_join_rows(x, txt, c.lens, out, d->batch, d->n_txt, d->n_img, d->d_model, st), "join_rows");
+    MOSS_TRY(launch_join_rows(x, txt, c.lens, h, d->batch, d->n_txt, d->n_img, d->d_model, st), "join_rows");
   }
   MOSS_TRY(launch_silu_cond(cond, reinterpret_cast<float*>(c.ws + c.L.s_cond), d->batch, d->d_model, st),
            "silu_cond");
   for (int i = 0; i < n_blocks; ++i) {
-    rc = run_block(c, &blocks[i], rope, out);
+    rc = run_block(c, &blocks[i], rope, h, i + 1 == n_blocks ? out : nullptr);
     if (rc != MOSS_OK) return rc;
   }
   return MOSS_OK;
@@ -353,14 +359,14 @@ int moss_stack_forward(const moss_dims* dims, int32_t n_blocks, const uint16_t* 
 }
 
 int moss_k_join_rows(int32_t batch, int32_t n_txt, int32_t n_img, int32_t d_model, const uint16_t* x,
-                     const uint16_t* txt, const int32_t* txt_len, uint16_t* out, hipStream_t stream) {
+                     const uint16_t* txt, const int32_t* txt_len, float* out, hipStream_t stream) {
   moss_dims d = {batch, n_img, n_txt, d_model, d_model / MOSS_HEAD_DIM, MOSS_HEAD_DIM, 128, 1e-6f};
   if (!dims_ok(&d)) return MOSS_EINVAL;
   ItemLens lens;
   if (!lens_ok(&d, txt_len, &lens)) return MOSS_EINVAL;
   if (!out || !aligned16(out) || (n_img > 0 && (!x || !aligned16(x))) || (n_txt > 0 && (!txt || !aligned16(txt))))
     return MOSS_EINVAL;
-  const size_t ob = 2ull * batch * (n_txt + n_img) * d_model;
+  const size_t ob = 4ull * batch * (n_txt + n_img) * d_model;
   if (overlaps(out, ob, x, 2ull * batch * n_img * d_model) || overlaps(out, ob, txt, 2ull * batch * n_txt * d_model))
     return MOSS_EALIAS;
   const int rc = single_device_check();
@@ -384,7 +390,7 @@ int moss_k_adaln_gemv(int32_t batch, int32_t d_model, const uint16_t* cond, cons
   return MOSS_OK;
 }
 
-int moss_k_mod_rmsnorm(int32_t batch, int32_t rows, int32_t d_model, float eps, const uint16_t* h,
+int moss_k_mod_rmsnorm(int32_t batch, int32_t rows, int32_t d_model, float eps, const float* h,
                        const float* shift, const float* scale, int32_t mod_stride, uint16_t* out,
                        hipStream_t stream) {
   if (batch < 1 || rows < 1 || (long)batch * rows > (long)MOSS_MAX_BATCH * MOSS_MAX_ROWS) return MOSS_EINVAL;
@@ -393,7 +399,7 @@ int moss_k_mod_rmsnorm(int32_t batch, int32_t rows, int32_t d_model, float eps, 
   if (mod_stride < d_model || mod_stride % 4) return MOSS_EINVAL;
   if (!h || !shift || !scale || !out || !aligned16(h) || !aligned16(shift) || !aligned16(scale) || !aligned16(out))
     return MOSS_EINVAL;
-  if (overlaps(out, 2ull * batch * rows * d_model, h, 2ull * batch * rows * d_model)) return MOSS_EALIAS;
+  if (overlaps(out, 2ull * batch * rows * d_model, h, 4ull * batch * rows * d_model)) return MOSS_EALIAS;
   const int rc = single_device_check();
   if (rc != MOSS_OK) return rc;
   MOSS_TRY(launch_mod_rmsnorm(h, shift, scale, mod_stride, out, batch, rows, d_model, eps, stream), "mod_rmsnorm");
@@ -465,18 +471,21 @@ int moss_k_silu_mul(int32_t rows, int32_t mlp_inner, const uint16_t* u, uint16_t
   return MOSS_OK;
 }
 
-int moss_k_gated_add(int32_t batch, int32_t rows, int32_t d_model, uint16_t* h, const float* gate,
-                     int32_t gate_stride, const uint16_t* y, hipStream_t stream) {
+int moss_k_gated_add(int32_t batch, int32_t rows, int32_t d_model, float* h, const float* gate,
+                     int32_t gate_stride, const uint16_t* y, uint16_t* out, hipStream_t stream) {
   if (batch < 1 || batch > MOSS_MAX_BATCH || rows < 1 || rows > MOSS_MAX_ROWS || d_model < 128 || d_model % 128 ||
       d_model > MOSS_MAX_DMODEL || gate_stride < d_model || gate_stride % 4)
     return MOSS_EINVAL;
-  if (!h || !gate || !y || !aligned16(h) || !aligned16(gate) || !aligned16(y)) return MOSS_EINVAL;
-  const size_t hb = 2ull * batch * rows * d_model;
-  if (overlaps(h, hb, y, hb) || overlaps(h, hb, gate, 4ull * ((size_t)(batch - 1) * gate_stride + d_model)))
+  if (!h || !gate || !y || !aligned16(h) || !aligned16(gate) || !aligned16(y) || (out && !aligned16(out)))
+    return MOSS_EINVAL;
+  const size_t hb = 4ull * batch * rows * d_model, yb = 2ull * batch * rows * d_model;
+  const size_t gb = 4ull * ((size_t)(batch - 1) * gate_stride + d_model);
+  if (overlaps(h, hb, y, yb) || overlaps(h, hb, gate, gb) ||
+      (out && (overlaps(out, yb, h, hb) || overlaps(out, yb, y, yb) || overlaps(out, yb, gate, gb))))
     return MOSS_EALIAS;
   const int rc = single_device_check();
   if (rc != MOSS_OK) return rc;
-  MOSS_TRY(launch_gated_add(h, gate, gate_stride, y, batch, rows, d_model, stream), "gated_add");
+  MOSS_TRY(launch_gated_add(h, gate, gate_stride, y, out, batch, rows, d_model, stream), "gated_add");
   return MOSS_OK;
 }
 

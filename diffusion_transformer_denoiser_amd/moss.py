@@ -60,7 +60,7 @@ _SIGS = {
                                                 c_vp, c_vp]),
     "moss_k_attention": (ctypes.c_int, [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moss_k_silu_mul": (ctypes.c_int, [c_i32, c_i32, c_vp, c_vp, c_vp]),
-    "moss_k_gated_add": (ctypes.c_int, [c_i32, c_i32, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp]),
+    "moss_k_gated_add": (ctypes.c_int, [c_i32, c_i32, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp]),
     "moss_probe_arm": (ctypes.c_int, [c_i32, c_i32]),
     "moss_probe_collect": (c_i32, [ctypes.POINTER(ctypes.c_float), c_i32]),
 }
@@ -208,8 +208,8 @@ def moss_k_silu_mul(rows, mlp_inner, u, z, stream=None) -> None:
     _check(lib().moss_k_silu_mul(rows, mlp_inner, _p(u), _p(z), _s(stream)), "moss_k_silu_mul")
 
 
-def moss_k_gated_add(batch, rows, d_model, h, gate, gate_stride, y, stream=None) -> None:
-    _check(lib().moss_k_gated_add(batch, rows, d_model, _p(h), _p(gate), gate_stride, _p(y), _s(stream)),
+def moss_k_gated_add(batch, rows, d_model, h, gate, gate_stride, y, out=None, stream=None) -> None:
+    _check(lib().moss_k_gated_add(batch, rows, d_model, _p(h), _p(gate), gate_stride, _p(y), _p(out), _s(stream)),
            "moss_k_gated_add")
 
 

@@ -176,6 +176,15 @@ def make_block_weights(geom: Geometry, seed: int = 0, block: int = 0, std: float
     }
 
 
+def normal_f32(seed: int, key: tuple, shape: tuple, std: float) -> np.ndarray:
+    """float32 values ``std * N(0, 1)`` from stream ``key`` (no bf16 rounding)."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=tuple(key) + (0,))))
+    v = g.standard_normal(n, dtype=np.float32)
+    v *= np.float32(std)
+    return v.reshape(shape)
+
+
 def make_tensor(seed: int, tag: int, shape: tuple, std: float = 1.0) -> np.ndarray:
     """An extra test tensor (bf16 bits) on activation stream ``(0, 3 + tag)``."""
     return normal_bf16(seed, (0, 3 + tag), shape, std)

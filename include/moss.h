@@ -121,7 +121,8 @@ int moss_rope_build(int32_t n_txt, int32_t grid_h, int32_t grid_w, float theta, 
  * rotary, O = softmax(q k^T / sqrt(128) + mask) v, h1 = h0 + gate1 (O W_out^T),
  * m = RMSNorm(h1) (1 + scale2) + shift2, u = m W_up^T, z = SiLU(u_gate) u_up,
  * out = h1 + gate2 (z W_down^T).  Each stored intermediate is rounded to bf16
- * (the modulation vector stays fp32). */
+ * except the modulation vector and the residual stream h0 -> h1 -> out, a
+ * running sum kept in fp32 and rounded once, into out. */
 int moss_block_forward(const moss_dims* dims, const uint16_t* x, const uint16_t* txt,
                        const int32_t* txt_len, const uint16_t* cond, const moss_block_weights* w,
                        const float* rope, uint16_t* out, void* workspace, size_t ws_bytes,
@@ -130,7 +131,8 @@ int moss_block_forward(const moss_dims* dims, const uint16_t* x, const uint16_t*
 /* n_blocks block forwards in sequence (blocks: host array of n_blocks weight
  * structs), each on the previous block's output, with the same cond, rope and
  * txt_len.  Arguments otherwise as moss_block_forward; `out` holds the
- * residual stream between blocks and the final output at the end. */
+ * final output; the residual stream between blocks stays in fp32 in the
+ * workspace. */
 int moss_stack_forward(const moss_dims* dims, int32_t n_blocks, const uint16_t* x, const uint16_t* txt,
                        const int32_t* txt_len, const uint16_t* cond, const moss_block_weights* blocks,
                        const float* rope, uint16_t* out, void* workspace, size_t ws_bytes,
@@ -147,9 +149,10 @@ int moss_stack_forward(const moss_dims* dims, int32_t n_blocks, const uint16_t* 
 int32_t moss_packed_rows(int32_t rows);
 
 /* a0: out[b, r] = r < n_txt ? (r < txt_len[b] ? txt[b, r] : 0) : x[b, r - n_txt];
- * out [B, T, D].  txt_len host or NULL. */
+ * x and txt bf16, out [B, T, D] fp32 (the residual stream the block keeps in
+ * fp32 between its gated adds).  txt_len host or NULL. */
 int moss_k_join_rows(int32_t batch, int32_t n_txt, int32_t n_img, int32_t d_model, const uint16_t* x,
-                     const uint16_t* txt, const int32_t* txt_len, uint16_t* out, hipStream_t stream);
+                     const uint16_t* txt, const int32_t* txt_len, float* out, hipStream_t stream);
 
 /* a1: mod[b, :] = W_mod SiLU(cond[b, :]) in fp32; cond [B, D], w_mod [6D, D],
  * mod [B, 6D] fp32.  Needs 4*B*D bytes of workspace for SiLU(cond). */
@@ -157,10 +160,11 @@ int moss_k_adaln_gemv(int32_t batch, int32_t d_model, const uint16_t* cond, cons
                       float* mod, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* a2/a8: out[b, r, :] = h[b, r, :] / sqrt(mean(h^2) + eps) * (1 + scale[b, :]) + shift[b, :];
- * h, out [B, rows, D] bf16; shift and scale fp32 with item stride mod_stride
- * floats (shift[b] at shift + b * mod_stride).  The modulated RMSNorm kernel
- * of the MOSS-Image transformer page ("What it adds"). */
-int moss_k_mod_rmsnorm(int32_t batch, int32_t rows, int32_t d_model, float eps, const uint16_t* h,
+ * h [B, rows, D] fp32 residual, out [B, rows, D] bf16; shift and scale fp32
+ * with item stride mod_stride floats (shift[b] at shift + b * mod_stride).
+ * The modulated RMSNorm kernel of the MOSS-Image transformer page ("What it
+ * adds"). */
+int moss_k_mod_rmsnorm(int32_t batch, int32_t rows, int32_t d_model, float eps, const float* h,
                        const float* shift, const float* scale, int32_t mod_stride, uint16_t* out,
                        hipStream_t stream);
 
@@ -195,11 +199,14 @@ int moss_k_attention(int32_t batch, int32_t n_heads, int32_t rows, int32_t n_txt
  * ("What it adds"). */
 int moss_k_silu_mul(int32_t rows, int32_t mlp_inner, const uint16_t* u, uint16_t* z, hipStream_t stream);
 
-/* a7/a12: h[b, r, :] = h[b, r, :] + gate[b, :] * y[b, r, :] in place (bf16 h and
- * y, fp32 gate with item stride gate_stride floats).  The gated add kernel of
- * the MOSS-Image transformer page ("What it adds"). */
-int moss_k_gated_add(int32_t batch, int32_t rows, int32_t d_model, uint16_t* h, const float* gate,
-                     int32_t gate_stride, const uint16_t* y, hipStream_t stream);
+/* a7/a12: h[b, r, :] + gate[b, :] * y[b, r, :] on the fp32 residual h, with
+ * y bf16 and gate fp32 (item stride gate_stride floats).  With out NULL the
+ * sum replaces h in place; otherwise it is rounded to bf16 into out [B, rows,
+ * D] and h is left unchanged (the last add of a call).  The gated add kernel
+ * of the MOSS-Image transformer page ("What it adds"); the residual is a
+ * running sum, kept in fp32 under the page's fp32-sums policy. */
+int moss_k_gated_add(int32_t batch, int32_t rows, int32_t d_model, float* h, const float* gate,
+                     int32_t gate_stride, const uint16_t* y, uint16_t* out, hipStream_t stream);
 
 /* ---- timing probe -------------------------------------------------------- */
 /* Step identifiers for the probe (the launches of moss_block_forward /

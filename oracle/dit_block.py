@@ -29,8 +29,11 @@ Headline mode computes every step exactly in float64 on the bf16 inputs
 widened exactly.  ``rounded=True`` rounds to bf16 (to float32 for the
 modulation vector and rotary tables) at each point where the GPU path stores a
 tensor, as the pages' kernel contract does ("float64 at the torch code's bf16
-rounding points", MOSS-Image encoder page PR #1512, "Receipt").  Pages'
-readings are cited per function.
+rounding points", MOSS-Image encoder page PR #1512, "Receipt").  The residual
+stream is a running sum of the blocks' gated contributions; under the fp32
+sums of the precision policy it is not rounded between the gated adds or
+between blocks, only when a call returns its output.  Pages' readings are
+cited per function.
 """
 from __future__ import annotations
 
@@ -253,12 +256,12 @@ def block_residual(h0, cond, txt_len, n_txt: int, w: dict, cos, sin, eps: float,
         o = r16(attention(q, k, v, valid[b], r16))
         o = o.transpose(1, 0, 2).reshape(t, d)
         o2 = r16(o @ w["w_out"].T)
-        h1 = r16(gated_add(h0[b], mb["gate1"], o2))
+        h1 = gated_add(h0[b], mb["gate1"], o2)
         m = r16(modulated_rmsnorm(h1, mb["shift2"], mb["scale2"], eps))
         u = r16(m @ w["w_up"].T)
         z = r16(silu_gate(u, f))
         y = r16(z @ w["w_down"].T)
-        out[b] = r16(gated_add(h1, mb["gate2"], y))
+        out[b] = gated_add(h1, mb["gate2"], y)
         if keep:
             for name, val in (("mod", mods[b]), ("a", a), ("qkv", qkv), ("q", q), ("k", k), ("v", v),
                               ("attn", o), ("o2", o2), ("h1", h1), ("m", m), ("u", u), ("z", z), ("y", y)):
@@ -272,9 +275,12 @@ def block_forward(x, txt, txt_len, cond, w: dict, cos, sin, eps: float = 1e-6,
                   rounded: bool = False, keep: bool = False):
     """Block output [B, n_txt + n_img, D] for image rows x and text rows txt."""
     h0 = join_rows(x, txt, txt_len)
-    if rounded:
-        h0 = round_bf16(h0)
-    return block_residual(h0, cond, txt_len, txt.shape[1], w, cos, sin, eps, rounded, keep)
+    res = block_residual(h0, cond, txt_len, txt.shape[1], w, cos, sin, eps, rounded, keep)
+    if not rounded:
+        return res
+    if keep:
+        return round_bf16(res[0]), res[1]
+    return round_bf16(res)
 
 
 def stack_forward(x, txt, txt_len, cond, blocks, cos, sin, eps: float = 1e-6,
@@ -288,11 +294,9 @@ def stack_forward(x, txt, txt_len, cond, blocks, cos, sin, eps: float = 1e-6,
     released model has more than 22 blocks.
     """
     h = join_rows(x, txt, txt_len)
-    if rounded:
-        h = round_bf16(h)
     for w in blocks:
         h = block_residual(h, cond, txt_len, txt.shape[1], w, cos, sin, eps, rounded)
-    return h
+    return round_bf16(h) if rounded else h
 
 
 def weights_f64(bits: dict) -> dict:

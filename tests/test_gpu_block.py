@@ -171,3 +171,49 @@ def test_stack_guidance_pair_two_blocks():
     got = G.host_f64(gpu_forward(geom, acts, ws))
     G.say("  oracle ...")
     check(geom, acts, got, oracle_forward(geom, acts, ws))
+
+
+def test_stack_guidance_pair_24_blocks():
+    """The full 24-block stack at the guidance-pair geometry against the oracle's sampled rows.
+
+    The expected rows were written by tests/golden/make_stack_golden.py, which
+    runs only the float64 oracle on the seeded inputs; the input digest
+    checks that the generator still draws the same bits.
+    """
+    import os
+    import sys
+    t = G.torch()
+    gold_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "stack24_c4_rows.npz")
+    gold = np.load(gold_path)
+    sys.path.insert(0, os.path.dirname(gold_path))
+    from make_stack_golden import input_digest
+
+    geom = synth.CONFIGS["c4"]
+    G.say(f"stack c4 x{geom.n_blocks}: generating inputs")
+    acts = synth.make_activations(geom, 0)
+    dims = G.geometry_dims(geom)
+    dev_w = []
+    for i in range(geom.n_blocks):
+        wb = synth.make_block_weights(geom, 0, i)
+        if i == 0:
+            assert input_digest(acts, wb) == str(gold["input_sha256"]), "seeded inputs differ from the golden's"
+        dev_w.append({k: G.dev(v) for k, v in wb.items()})
+    rope = G.empty_f32(2, geom.rows, 64)
+    moss.moss_rope_build(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, rope)
+    ws = t.empty(moss.moss_workspace_bytes(dims, geom.n_blocks), dtype=t.uint8, device="cuda")
+    out = G.empty_bf16(geom.batch, geom.rows, geom.d_model)
+    G.say("  stack forward")
+    moss.moss_stack_forward(dims, dev_w, G.dev(acts["x"]), G.dev(acts["txt"]), acts["txt_len"], G.dev(acts["cond"]),
+                            rope, out, ws)
+    G.sync()
+    full = G.host_f64(out)
+    rows = gold["rows"]
+    got = full[:, rows, :]
+    ref = gold["values"].astype(np.float64)
+    h0 = ob.join_rows(ob.widen_bf16(acts["x"]), ob.widen_bf16(acts["txt"]), acts["txt_len"])[:, rows, :]
+    for b in range(geom.batch):
+        G.assert_parity(f"item {b} rows", got[b], ref[b])
+        G.assert_parity(f"item {b} rows - h0", got[b] - h0[b], ref[b] - h0[b])
+    rms = np.sqrt(np.mean(full * full, axis=(1, 2)))
+    G.say(f"  item rms {rms} vs {gold['item_rms']}")
+    assert np.allclose(rms, gold["item_rms"], rtol=2e-3)

@@ -51,11 +51,11 @@ def test_join_rows_pad_rows_are_zero():
     txt[1, 3:] = 0x3F80  # pad rows hold 1.0: must not be read
     txt[2, :] = 0x4000
     G.say("join_rows B=3 txt_len=(8,3,0)")
-    out = G.empty_bf16(3, geom.rows, geom.d_model)
+    out = G.empty_f32(3, geom.rows, geom.d_model)
     moss.moss_k_join_rows(3, geom.n_txt, geom.n_img, geom.d_model, G.dev(acts["x"]), G.dev(txt), acts["txt_len"], out)
     G.sync()
     ref = ob.join_rows(ob.widen_bf16(acts["x"]), ob.widen_bf16(txt), acts["txt_len"])
-    np.testing.assert_array_equal(G.host_f64(out), ref)
+    np.testing.assert_array_equal(out.cpu().numpy().astype(np.float64), ref)
 
 
 # ---- a1 adaLN GEMV ----------------------------------------------------------------------------
@@ -78,17 +78,17 @@ def test_adaln_gemv(batch, d):
 
 # ---- a2/a8 modulated RMSNorm ------------------------------------------------------------------
 
-@pytest.mark.parametrize("batch,rows,d", [(1, 72, 256), (2, 130, 3072), (1, 33, 8192), (3, 5, 384)])
+@pytest.mark.parametrize("batch,rows,d", [(1, 72, 256), (2, 130, 3072), (1, 33, 8192), (3, 5, 384), (1, 9, 1152)])
 def test_mod_rmsnorm(batch, rows, d):
     G.say(f"mod_rmsnorm B={batch} rows={rows} D={d}")
-    h = synth.make_tensor(3, 0, (batch, rows, d), std=1.5)
+    h = synth.normal_f32(3, (0, 60), (batch, rows, d), 1.5)
     mod = ob.widen_bf16(synth.make_tensor(3, 1, (batch, 6 * d), std=0.7)).astype(np.float32)
     out = G.empty_bf16(batch, rows, d)
     mod_d = G.dev_f32(mod)
-    moss.moss_k_mod_rmsnorm(batch, rows, d, 1e-6, G.dev(h), mod_d[:, 3 * d:], mod_d[:, 4 * d:], 6 * d, out)
+    moss.moss_k_mod_rmsnorm(batch, rows, d, 1e-6, G.dev_f32(h), mod_d[:, 3 * d:], mod_d[:, 4 * d:], 6 * d, out)
     G.sync()
     m = mod.astype(np.float64)
-    ref = ob.modulated_rmsnorm(ob.widen_bf16(h), m[:, None, 3 * d:4 * d], m[:, None, 4 * d:5 * d], 1e-6)
+    ref = ob.modulated_rmsnorm(h.astype(np.float64), m[:, None, 3 * d:4 * d], m[:, None, 4 * d:5 * d], 1e-6)
     G.assert_ulps("a", G.host_f64(out), ref, ulps=1.0, abs_floor=1e-5)
 
 
@@ -249,14 +249,23 @@ def test_silu_mul(rows, f):
 
 
 @pytest.mark.parametrize("batch,rows,d", [(1, 72, 256), (2, 4130, 3072), (3, 9, 384)])
-def test_gated_add(batch, rows, d):
-    G.say(f"gated_add B={batch} rows={rows} D={d}")
-    h = synth.make_tensor(11, 0, (batch, rows, d))
+@pytest.mark.parametrize("to_bf16", [False, True])
+def test_gated_add(batch, rows, d, to_bf16):
+    G.say(f"gated_add B={batch} rows={rows} D={d} bf16 out={to_bf16}")
+    h = synth.normal_f32(11, (0, 61), (batch, rows, d), 1.0)
     y = synth.make_tensor(11, 1, (batch, rows, d), std=0.8)
     gate = ob.widen_bf16(synth.make_tensor(11, 2, (batch, 6 * d), std=0.7)).astype(np.float32)
-    hd = G.dev(h)
+    hd = G.dev_f32(h)
     gd = G.dev_f32(gate)
-    moss.moss_k_gated_add(batch, rows, d, hd, gd[:, 2 * d:], 6 * d, G.dev(y))
+    out = G.empty_bf16(batch, rows, d) if to_bf16 else None
+    moss.moss_k_gated_add(batch, rows, d, hd, gd[:, 2 * d:], 6 * d, G.dev(y), out)
     G.sync()
-    ref = ob.gated_add(ob.widen_bf16(h), gate.astype(np.float64)[:, None, 2 * d:3 * d], ob.widen_bf16(y))
-    G.assert_ulps("h", G.host_f64(hd), ref, ulps=0.5, abs_floor=1e-6)
+    ref = ob.gated_add(h.astype(np.float64), gate.astype(np.float64)[:, None, 2 * d:3 * d], ob.widen_bf16(y))
+    if to_bf16:
+        G.assert_ulps("out", G.host_f64(out), ref, ulps=0.5, abs_floor=1e-6)
+        np.testing.assert_array_equal(hd.cpu().numpy(), h)  # h untouched
+    else:
+        got = hd.cpu().numpy().astype(np.float64)
+        # one fp32 multiply-add: within 2^-23 of the larger of |h| and |gate * y|
+        bound = 2.0 ** -23 * (np.abs(ref) + np.abs(gate.astype(np.float64)[:, None, 2 * d:3 * d] * ob.widen_bf16(y)))
+        assert np.all(np.abs(got - ref) <= bound + 1e-30)
