@@ -24,6 +24,17 @@
 //    second, so a lane's accumulators hold runs of four consecutive output
 //    columns of one row and leave in 8-byte stores.
 // There is no split-K and no atomic: results are identical call to call.
+//
+// Epilogues (the MOSS-Image transformer page's SiLU and gated-add kernels,
+// "What it adds", applied to the fp32 sums before any rounding):
+//  * kStore: c = bf16(acc).
+//  * kSiluGate (the up projection, w = [gate rows; up rows], n = 2F): the
+//    weight tile of column tile t holds gate rows and up rows of the same
+//    128 outputs, interleaved per 32 so that one lane owns both sums of an
+//    output; c[:, F-wide] = bf16(SiLU(gate) * up).  u is never stored.
+//  * kGatedAdd (the out and down projections): h[r, :] += gate[b, :] * acc on
+//    the fp32 residual, or, for the last add of a call, out = bf16(h + gate *
+//    acc) with h unchanged.  The projection output is never stored.
 #include "common.h"
 #include "launch.h"
 
@@ -31,6 +42,16 @@ namespace {
 
 constexpr int KB = 32;      // k per slab
 constexpr int STAGES = 4;   // LDS ring depth
+
+enum Epi { kStore = 0, kSiluGate = 1, kGatedAdd = 2 };
+
+struct EpiArgs {
+  float* h;           // kGatedAdd: fp32 residual [m, n], row stride n
+  const float* gate;  // kGatedAdd: gate of item b at gate + b * gate_stride
+  int gate_stride;
+  int rows_per_item;
+  uint16_t* out16;    // kGatedAdd: when set, bf16 result here instead of updating h
+};
 
 // Workgroup id -> (tile_m, tile_n), M fastest, a contiguous run of tiles per XCD.
 __device__ __forceinline__ void tile_of(int id, int nblk, int mt, int& tm, int& tn) {
@@ -41,11 +62,11 @@ __device__ __forceinline__ void tile_of(int id, int nblk, int mt, int& tm, int& 
   tn = logical / mt;
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __restrict__ a, int lda,
                                                              const uint16_t* __restrict__ w, int ldw,
                                                              uint16_t* __restrict__ c, int ldc, int m, int n,
-                                                             int k) {
+                                                             int k, EpiArgs ep) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
@@ -53,6 +74,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
   constexpr int LA = AB / 1024 / NW, LB = BB / 1024 / NW;    // 1 KiB load instructions per wavefront
   constexpr int PER = LA + LB;
   static_assert(LA * NW * 1024 == AB && LB * NW * 1024 == BB, "slab / wavefront mismatch");
+  static_assert(EPI != kSiluGate || FN == 2, "the SiLU epilogue pairs a gate and an up fragment per wavefront");
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * (AB + BB)];
 
   const int mt = (m + BM - 1) / BM;
@@ -75,7 +97,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
     const int r = (wave + NW * i) * 16 + (lane >> 2);
-    gb[i] = w + (size_t)(n0 + r) * ldw + ((lane & 3) ^ ((r >> 2) & 3)) * 8;
+    int wrow = n0 + r;
+    if (EPI == kSiluGate) {
+      // tile row r -> wavefront r / TN, fragment (r % TN) / 32: fragment 0 = gate rows, 1 = up rows
+      const int zc = tn * (BN / 2) + (r / TN) * 32 + (r & 31);
+      wrow = ((r % TN) >= 32 ? n / 2 : 0) + zc;
+    }
+    gb[i] = w + (size_t)wrow * ldw + ((lane & 3) ^ ((r >> 2) & 3)) * 8;
   }
   auto issue = [&](int slab) {
     MOSS_LDS char* base = (MOSS_LDS char*)smem + (slab % STAGES) * (AB + BB);
@@ -153,7 +181,41 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
     const int row = m0 + wm * TM + j * 32 + l32;
-    if (row < m) {
+    if (row >= m) continue;
+    if (EPI == kSiluGate) {
+      uint16_t* crow = c + (size_t)row * ldc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = tn * (BN / 2) + wn * 32 + 8 * q + 4 * hh;
+        float z[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[e] = silu_f32(acc[0][j][4 * q + e]) * acc[1][j][4 * q + e];
+        u32x2 v = {pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+        *reinterpret_cast<u32x2*>(crow + col) = v;
+      }
+    } else if (EPI == kGatedAdd) {
+      const int b = row / ep.rows_per_item;
+      const float* g = ep.gate + (size_t)b * ep.gate_stride;
+      float* hrow = ep.h + (size_t)row * n;
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + wn * TN + i * 32 + 8 * q + 4 * hh;
+          const f32x4 g4 = *reinterpret_cast<const f32x4*>(g + col);
+          const f32x4 h4 = *reinterpret_cast<const f32x4*>(hrow + col);
+          f32x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = h4[e] + g4[e] * acc[i][j][4 * q + e];
+          if (ep.out16) {
+            u32x2 v = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+            *reinterpret_cast<u32x2*>(ep.out16 + (size_t)row * n + col) = v;
+          } else {
+            *reinterpret_cast<f32x4*>(hrow + col) = o;
+          }
+        }
+      }
+    } else {
       uint16_t* crow = c + (size_t)row * ldc;
 #pragma unroll
       for (int i = 0; i < FN; ++i) {
@@ -169,17 +231,35 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
   }
 }
 
+template <int EPI>
+hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_t* w, int ldw, uint16_t* c, int ldc,
+                  const EpiArgs& ep, hipStream_t st) {
+  const int mt = (m + 255) / 256;
+  if (n % 256 == 0) {
+    hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI>), dim3(mt * (n / 256)), dim3(512), 0, st, a, lda, w, ldw,
+                       c, ldc, m, n, k, ep);
+  } else {
+    hipLaunchKernelGGL((gemm_nt_kernel<256, 128, 4, 2, EPI>), dim3(mt * (n / 128)), dim3(512), 0, st, a, lda, w, ldw,
+                       c, ldc, m, n, k, ep);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_nt(int m, int n, int k, const uint16_t* a, int lda, const uint16_t* w, int ldw,
                           uint16_t* c, int ldc, hipStream_t st) {
-  const int mt = (m + 255) / 256;
-  if (n % 256 == 0) {
-    hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4>), dim3(mt * (n / 256)), dim3(512), 0, st, a, lda, w, ldw, c,
-                       ldc, m, n, k);
-  } else {
-    hipLaunchKernelGGL((gemm_nt_kernel<256, 128, 4, 2>), dim3(mt * (n / 128)), dim3(512), 0, st, a, lda, w, ldw, c,
-                       ldc, m, n, k);
-  }
-  return hipGetLastError();
+  return launch<kStore>(m, n, k, a, lda, w, ldw, c, ldc, EpiArgs{}, st);
+}
+
+hipError_t launch_gemm_silu(int m, int f, int k, const uint16_t* a, int lda, const uint16_t* w_up, int ldw,
+                            uint16_t* z, int ldz, hipStream_t st) {
+  return launch<kSiluGate>(m, 2 * f, k, a, lda, w_up, ldw, z, ldz, EpiArgs{}, st);
+}
+
+hipError_t launch_gemm_gated_add(int m, int n, int k, const uint16_t* a, int lda, const uint16_t* w, int ldw,
+                                 float* h, const float* gate, int gate_stride, int rows_per_item, uint16_t* out16,
+                                 hipStream_t st) {
+  const EpiArgs ep{h, gate, gate_stride, rows_per_item, out16};
+  return launch<kGatedAdd>(m, n, k, a, lda, w, ldw, nullptr, n, ep, st);
 }

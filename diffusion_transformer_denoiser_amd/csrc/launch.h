@@ -23,6 +23,16 @@ hipError_t launch_rope_build(int n_txt, int grid_h, int grid_w, float theta, flo
 hipError_t launch_gemm_nt(int m, int n, int k, const uint16_t* a, int lda, const uint16_t* w, int ldw,
                           uint16_t* c, int ldc, hipStream_t st);
 
+// z[m, f] = SiLU(a w_up[j]^T) * (a w_up[f + j]^T) for w_up = [gate rows; up rows] [2f, k].
+// f % 128 == 0 (and 2f % 256 == 0 for the 256-wide tiles the pairing needs).
+hipError_t launch_gemm_silu(int m, int f, int k, const uint16_t* a, int lda, const uint16_t* w_up, int ldw,
+                            uint16_t* z, int ldz, hipStream_t st);
+// h[r, :] += gate[r / rows_per_item, :] * (a w^T)[r, :] on the fp32 residual h [m, n];
+// with out16 set, out16 = bf16(h + gate * a w^T) and h is left unchanged.
+hipError_t launch_gemm_gated_add(int m, int n, int k, const uint16_t* a, int lda, const uint16_t* w, int ldw,
+                                 float* h, const float* gate, int gate_stride, int rows_per_item, uint16_t* out16,
+                                 hipStream_t st);
+
 // Rows of the packed attention layouts: rows rounded up to a multiple of 128.
 inline int packed_rows(int rows) { return (rows + 127) / 128 * 128; }
 

@@ -59,15 +59,17 @@ bool lens_ok(const moss_dims* d, const int32_t* txt_len, ItemLens* out) {
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t s_cond, mod, h, a, y, qkv, qp, kp, vp, u, z, total;
+  size_t s_cond, mod, h, a, qkv, qp, kp, vp, z, total;
 };
 
 // Offsets (bytes) into the workspace.  h is the fp32 residual stream (the
 // running sum of the gated adds, rounded to bf16 only when `out` is written).
-// a holds the first norm's output, then
-// the attention output, then the second norm's output; y holds each
-// projection output that is added to the residual; the union region holds the
-// qkv rows and packed q/k/v during attention, and the MLP activations after.
+// a holds the first norm's output, then the attention output, then the second
+// norm's output.  One union region holds the qkv rows and packed q/k/v during
+// attention, and the MLP activation z after.  The projection outputs added to
+// the residual and the up projection's output never reach memory: the out and
+// down projections add into h in their epilogues, and the up projection
+// applies the SiLU gate in its epilogue.
 Layout plan(const moss_dims* d) {
   Layout L;
   const size_t B = d->batch, T = (size_t)d->n_txt + d->n_img, D = d->d_model, F = d->mlp_inner;
@@ -82,7 +84,6 @@ Layout plan(const moss_dims* d) {
   L.mod = take(4 * B * 6 * D);
   L.h = take(4 * R * D);
   L.a = take(2 * R * D);
-  L.y = take(2 * R * D);
   const size_t base = off;
   const size_t packed = round256(2 * B * H * Tp * 128);
   L.qkv = base;
@@ -90,8 +91,7 @@ Layout plan(const moss_dims* d) {
   L.kp = L.qp + packed;
   L.vp = L.kp + packed;
   const size_t end1 = L.vp + packed;
-  L.u = base;
-  L.z = base + round256(2 * R * 2 * F);
+  L.z = base;
   const size_t end2 = L.z + round256(2 * R * F);
   L.total = end1 > end2 ? end1 : end2;
   return L;
@@ -181,12 +181,10 @@ int run_block(const Ctx& c, const moss_block_weights* w, const float* rope, floa
   float* s = reinterpret_cast<float*>(c.ws + c.L.s_cond);
   float* mod = reinterpret_cast<float*>(c.ws + c.L.mod);
   uint16_t* a = reinterpret_cast<uint16_t*>(c.ws + c.L.a);
-  uint16_t* y = reinterpret_cast<uint16_t*>(c.ws + c.L.y);
   uint16_t* qkv = reinterpret_cast<uint16_t*>(c.ws + c.L.qkv);
   uint16_t* qp = reinterpret_cast<uint16_t*>(c.ws + c.L.qp);
   uint16_t* kp = reinterpret_cast<uint16_t*>(c.ws + c.L.kp);
   uint16_t* vp = reinterpret_cast<uint16_t*>(c.ws + c.L.vp);
-  uint16_t* u = reinterpret_cast<uint16_t*>(c.ws + c.L.u);
   uint16_t* z = reinterpret_cast<uint16_t*>(c.ws + c.L.z);
   const int ms = 6 * D;  // item stride of the modulation vector
   hipStream_t st = c.st;
@@ -212,32 +210,22 @@ int run_block(const Ctx& c, const moss_block_weights* w, const float* rope, floa
     MOSS_TRY(launch_attention(B, H, T, d->n_txt, c.lens, qp, kp, vp, a, st), "attention");
   }
   {
-    StepTimer t(MOSS_STEP_OUT, st);
-    MOSS_TRY(launch_gemm_nt(R, D, D, a, D, w->w_out, D, y, D, st), "gemm out");
-  }
-  {
-    StepTimer t(MOSS_STEP_GATE1, st);
-    MOSS_TRY(launch_gated_add(h, mod + 2 * D, ms, y, nullptr, B, T, D, st), "gated_add");
+    StepTimer t(MOSS_STEP_OUT, st);  // out projection + first gated add
+    MOSS_TRY(launch_gemm_gated_add(R, D, D, a, D, w->w_out, D, h, mod + 2 * D, ms, T, nullptr, st),
+             "gemm out + gated add");
   }
   {
     StepTimer t(MOSS_STEP_NORM2, st);
     MOSS_TRY(launch_mod_rmsnorm(h, mod + 3 * D, mod + 4 * D, ms, a, B, T, D, d->eps, st), "mod_rmsnorm");
   }
   {
-    StepTimer t(MOSS_STEP_UP, st);
-    MOSS_TRY(launch_gemm_nt(R, 2 * F, D, a, D, w->w_up, D, u, 2 * F, st), "gemm up");
+    StepTimer t(MOSS_STEP_UP, st);  // up projection + SiLU gate
+    MOSS_TRY(launch_gemm_silu(R, F, D, a, D, w->w_up, D, z, F, st), "gemm up + silu");
   }
   {
-    StepTimer t(MOSS_STEP_SILU, st);
-    MOSS_TRY(launch_silu_mul(u, z, R, F, st), "silu_mul");
-  }
-  {
-    StepTimer t(MOSS_STEP_DOWN, st);
-    MOSS_TRY(launch_gemm_nt(R, D, F, z, F, w->w_down, F, y, D, st), "gemm down");
-  }
-  {
-    StepTimer t(MOSS_STEP_GATE2, st);
-    MOSS_TRY(launch_gated_add(h, mod + 5 * D, ms, y, out16, B, T, D, st), "gated_add");
+    StepTimer t(MOSS_STEP_DOWN, st);  // down projection + second gated add
+    MOSS_TRY(launch_gemm_gated_add(R, D, F, z, F, w->w_down, F, h, mod + 5 * D, ms, T, out16, st),
+             "gemm down + gated add");
   }
   return MOSS_OK;
 }
@@ -486,6 +474,46 @@ int moss_k_gated_add(int32_t batch, int32_t rows, int32_t d_model, float* h, con
   const int rc = single_device_check();
   if (rc != MOSS_OK) return rc;
   MOSS_TRY(launch_gated_add(h, gate, gate_stride, y, out, batch, rows, d_model, stream), "gated_add");
+  return MOSS_OK;
+}
+
+int moss_k_gemm_silu(int32_t m, int32_t mlp_inner, int32_t k, const uint16_t* a, int32_t lda, const uint16_t* w_up,
+                     int32_t ldw, uint16_t* z, int32_t ldz, hipStream_t stream) {
+  if (m < 1 || mlp_inner < 128 || mlp_inner % 128 || k < 128 || k % 128) return MOSS_EINVAL;
+  if (lda < k || ldw < k || ldz < mlp_inner || lda % 8 || ldw % 8 || ldz % 8) return MOSS_EINVAL;
+  if ((long)m > (long)MOSS_MAX_BATCH * MOSS_MAX_ROWS) return MOSS_EINVAL;
+  if (!a || !w_up || !z || !aligned16(a) || !aligned16(w_up) || !aligned16(z)) return MOSS_EINVAL;
+  const size_t zb = 2ull * ((size_t)(m - 1) * ldz + mlp_inner);
+  if (overlaps(z, zb, a, 2ull * ((size_t)(m - 1) * lda + k)) ||
+      overlaps(z, zb, w_up, 2ull * ((size_t)(2 * mlp_inner - 1) * ldw + k)))
+    return MOSS_EALIAS;
+  const int rc = single_device_check();
+  if (rc != MOSS_OK) return rc;
+  MOSS_TRY(launch_gemm_silu(m, mlp_inner, k, a, lda, w_up, ldw, z, ldz, stream), "gemm_silu");
+  return MOSS_OK;
+}
+
+int moss_k_gemm_gated_add(int32_t m, int32_t n, int32_t k, const uint16_t* a, int32_t lda, const uint16_t* w,
+                          int32_t ldw, float* h, const float* gate, int32_t gate_stride, int32_t rows_per_item,
+                          uint16_t* out, hipStream_t stream) {
+  if (m < 1 || n < 128 || n % 128 || k < 128 || k % 128 || lda < k || ldw < k || lda % 8 || ldw % 8)
+    return MOSS_EINVAL;
+  if (rows_per_item < 1 || m % rows_per_item || m / rows_per_item > MOSS_MAX_BATCH) return MOSS_EINVAL;
+  if (gate_stride < n || gate_stride % 4) return MOSS_EINVAL;
+  if (!a || !w || !h || !gate || !aligned16(a) || !aligned16(w) || !aligned16(h) || !aligned16(gate) ||
+      (out && !aligned16(out)))
+    return MOSS_EINVAL;
+  const size_t hb = 4ull * m * n, ob = 2ull * m * n;
+  const size_t gb = 4ull * ((size_t)(m / rows_per_item - 1) * gate_stride + n);
+  const size_t ab = 2ull * ((size_t)(m - 1) * lda + k), wb = 2ull * ((size_t)(n - 1) * ldw + k);
+  if (overlaps(h, hb, a, ab) || overlaps(h, hb, w, wb) || overlaps(h, hb, gate, gb) ||
+      (out && (overlaps(out, ob, h, hb) || overlaps(out, ob, a, ab) || overlaps(out, ob, w, wb) ||
+               overlaps(out, ob, gate, gb))))
+    return MOSS_EALIAS;
+  const int rc = single_device_check();
+  if (rc != MOSS_OK) return rc;
+  MOSS_TRY(launch_gemm_gated_add(m, n, k, a, lda, w, ldw, h, gate, gate_stride, rows_per_item, out, stream),
+           "gemm_gated_add");
   return MOSS_OK;
 }
 

@@ -61,6 +61,9 @@ _SIGS = {
     "moss_k_attention": (ctypes.c_int, [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moss_k_silu_mul": (ctypes.c_int, [c_i32, c_i32, c_vp, c_vp, c_vp]),
     "moss_k_gated_add": (ctypes.c_int, [c_i32, c_i32, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp]),
+    "moss_k_gemm_silu": (ctypes.c_int, [c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_i32, c_vp, c_i32, c_vp]),
+    "moss_k_gemm_gated_add": (ctypes.c_int, [c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32,
+                                             c_vp, c_vp]),
     "moss_probe_arm": (ctypes.c_int, [c_i32, c_i32]),
     "moss_probe_collect": (c_i32, [ctypes.POINTER(ctypes.c_float), c_i32]),
 }
@@ -76,7 +79,9 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is not built; run `python -m diffusion_transformer_denoiser_amd.build`")
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
-            fn = getattr(handle, name)
+            fn = getattr(handle, name, None)
+            if fn is None:  # an older build: calling this entry point raises AttributeError
+                continue
             fn.restype = res
             fn.argtypes = args
         _lib = handle
@@ -211,6 +216,17 @@ def moss_k_silu_mul(rows, mlp_inner, u, z, stream=None) -> None:
 def moss_k_gated_add(batch, rows, d_model, h, gate, gate_stride, y, out=None, stream=None) -> None:
     _check(lib().moss_k_gated_add(batch, rows, d_model, _p(h), _p(gate), gate_stride, _p(y), _p(out), _s(stream)),
            "moss_k_gated_add")
+
+
+def moss_k_gemm_silu(m, mlp_inner, k, a, lda, w_up, ldw, z, ldz, stream=None) -> None:
+    _check(lib().moss_k_gemm_silu(m, mlp_inner, k, _p(a), lda, _p(w_up), ldw, _p(z), ldz, _s(stream)),
+           "moss_k_gemm_silu")
+
+
+def moss_k_gemm_gated_add(m, n, k, a, lda, w, ldw, h, gate, gate_stride, rows_per_item, out=None,
+                          stream=None) -> None:
+    _check(lib().moss_k_gemm_gated_add(m, n, k, _p(a), lda, _p(w), ldw, _p(h), _p(gate), gate_stride, rows_per_item,
+                                       _p(out), _s(stream)), "moss_k_gemm_gated_add")
 
 
 def moss_probe_arm(step, max_launches) -> None:

@@ -120,8 +120,10 @@ int moss_rope_build(int32_t n_txt, int32_t grid_h, int32_t grid_w, float theta, 
  * (1 + scale1) + shift1, qkv = a W_qkv^T, per head q/k RMSNorm x gain and
  * rotary, O = softmax(q k^T / sqrt(128) + mask) v, h1 = h0 + gate1 (O W_out^T),
  * m = RMSNorm(h1) (1 + scale2) + shift2, u = m W_up^T, z = SiLU(u_gate) u_up,
- * out = h1 + gate2 (z W_down^T).  Each stored intermediate is rounded to bf16
- * except the modulation vector and the residual stream h0 -> h1 -> out, a
+ * out = h1 + gate2 (z W_down^T).  Each stored intermediate (a, qkv, q/k/v,
+ * O, m, z) is rounded to bf16; the modulation vector is fp32; the projection
+ * outputs feeding the gated adds and the SiLU gate stay fp32 (they are
+ * consumed in the GEMM epilogues); the residual stream h0 -> h1 -> out is a
  * running sum kept in fp32 and rounded once, into out. */
 int moss_block_forward(const moss_dims* dims, const uint16_t* x, const uint16_t* txt,
                        const int32_t* txt_len, const uint16_t* cond, const moss_block_weights* w,
@@ -194,6 +196,27 @@ int moss_k_attention(int32_t batch, int32_t n_heads, int32_t rows, int32_t n_txt
                      const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                      hipStream_t stream);
 
+/* a9 + a10 as the block runs them: z[r, j] = SiLU((a w_up^T)[r, j]) * (a w_up^T)[r, F + j],
+ * a [m, k] (row stride lda), w_up [2F, k] gate rows then up rows (row stride
+ * ldw), z [m, F] bf16 (row stride ldz); fp32 sums and SiLU, one bf16
+ * rounding.  mlp_inner and k multiples of 128.  The bf16 GEMM and SiLU
+ * kernels of the MOSS-Image transformer page ("What it adds"), fused so the
+ * 2F-wide product never reaches memory. */
+int moss_k_gemm_silu(int32_t m, int32_t mlp_inner, int32_t k, const uint16_t* a, int32_t lda, const uint16_t* w_up,
+                     int32_t ldw, uint16_t* z, int32_t ldz, hipStream_t stream);
+
+/* a6 + a7 and a11 + a12 as the block runs them: h[r, :] += gate[b, :] * (a w^T)[r, :]
+ * with b = r / rows_per_item, on the fp32 residual h [m, n] (row stride n);
+ * a [m, k] (row stride lda), w [n, k] (row stride ldw), gate fp32 with item
+ * stride gate_stride floats.  With out not NULL the sum is rounded to bf16
+ * into out [m, n] and h is left unchanged.  n and k multiples of 128; m a
+ * multiple of rows_per_item, with at most MOSS_MAX_BATCH items.  The GEMM and
+ * gated-add kernels of the MOSS-Image transformer page ("What it adds"),
+ * fused so the projection output never reaches memory. */
+int moss_k_gemm_gated_add(int32_t m, int32_t n, int32_t k, const uint16_t* a, int32_t lda, const uint16_t* w,
+                          int32_t ldw, float* h, const float* gate, int32_t gate_stride, int32_t rows_per_item,
+                          uint16_t* out, hipStream_t stream);
+
 /* a10: z[r, c] = SiLU(u[r, c]) * u[r, F + c] for u [R, 2F], z [R, F] (bf16,
  * fp32 arithmetic).  The SiLU kernel of the MOSS-Image transformer page
  * ("What it adds"). */
@@ -210,7 +233,10 @@ int moss_k_gated_add(int32_t batch, int32_t rows, int32_t d_model, float* h, con
 
 /* ---- timing probe -------------------------------------------------------- */
 /* Step identifiers for the probe (the launches of moss_block_forward /
- * moss_stack_forward, in order). */
+ * moss_stack_forward, in order).  The gated adds and the SiLU gate run in the
+ * epilogues of the out, down and up projections: MOSS_STEP_OUT, _UP and _DOWN
+ * time the fused launches, and MOSS_STEP_GATE1, _SILU and _GATE2 record
+ * nothing. */
 #define MOSS_STEP_JOIN 0
 #define MOSS_STEP_ADALN 1
 #define MOSS_STEP_NORM1 2

@@ -32,8 +32,10 @@ tensor, as the pages' kernel contract does ("float64 at the torch code's bf16
 rounding points", MOSS-Image encoder page PR #1512, "Receipt").  The residual
 stream is a running sum of the blocks' gated contributions; under the fp32
 sums of the precision policy it is not rounded between the gated adds or
-between blocks, only when a call returns its output.  Pages' readings are
-cited per function.
+between blocks, only when a call returns its output.  The outputs of the
+out, up and down projections are consumed where they are produced (by the
+gated adds and the SiLU gate) and are not rounded either.  Pages' readings
+are cited per function.
 """
 from __future__ import annotations
 
@@ -255,12 +257,12 @@ def block_residual(h0, cond, txt_len, n_txt: int, w: dict, cos, sin, eps: float,
         v = heads[2]
         o = r16(attention(q, k, v, valid[b], r16))
         o = o.transpose(1, 0, 2).reshape(t, d)
-        o2 = r16(o @ w["w_out"].T)
+        o2 = o @ w["w_out"].T
         h1 = gated_add(h0[b], mb["gate1"], o2)
         m = r16(modulated_rmsnorm(h1, mb["shift2"], mb["scale2"], eps))
-        u = r16(m @ w["w_up"].T)
+        u = m @ w["w_up"].T
         z = r16(silu_gate(u, f))
-        y = r16(z @ w["w_down"].T)
+        y = z @ w["w_down"].T
         out[b] = gated_add(h1, mb["gate2"], y)
         if keep:
             for name, val in (("mod", mods[b]), ("a", a), ("qkv", qkv), ("q", q), ("k", k), ("v", v),

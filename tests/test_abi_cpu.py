@@ -63,8 +63,8 @@ def test_status_strings():
 def test_workspace_bytes():
     d = c2_dims()
     ws = moss.moss_workspace_bytes(d, 1)
-    # fp32 residual (50.7 MB) + a and y (25.4 MB each) + the MLP union (u 203 MB + z 101 MB) + small
-    assert 400 * MB < ws < 410 * MB, ws
+    # fp32 residual (50.7 MB) + a (25.4 MB) + the union of {qkv 76.1 MB + packed q/k/v 77.9 MB} and z (101.5 MB)
+    assert 225 * MB < ws < 235 * MB, ws
     assert moss.moss_workspace_bytes(d, 24) == ws
     assert moss.moss_workspace_bytes(c2_dims(batch=2), 1) > ws
     assert moss.moss_workspace_bytes(c2_dims(head_dim=64), 1) == 0
@@ -160,6 +160,18 @@ def test_single_step_entry_points_validate():
     assert L.moss_k_adaln_gemv(1, 256, fake(1), fake(2), fake(3), fake(4), 100, None) == moss.MOSS_EWORKSPACE
     assert L.moss_rope_build(-1, 4, 4, 10000.0, fake(1), None) == moss.MOSS_EINVAL
     assert L.moss_rope_build(2, 4, 4, 1.0, fake(1), None) == moss.MOSS_EINVAL
+
+
+def test_fused_gemm_entry_points_validate():
+    L = moss.lib()
+    assert L.moss_k_gemm_silu(100, 200, 256, fake(1), 256, fake(2), 256, fake(3), 200, None) == moss.MOSS_EINVAL
+    assert L.moss_k_gemm_silu(100, 256, 256, fake(1), 256, fake(2), 256, fake(2, 4096), 256, None) == moss.MOSS_EALIAS
+    assert L.moss_k_gemm_gated_add(100, 256, 256, fake(1), 256, fake(2), 256, fake(3), fake(4), 1536, 30, None,
+                                   None) == moss.MOSS_EINVAL  # 100 rows are not whole items of 30
+    assert L.moss_k_gemm_gated_add(100, 256, 256, fake(1), 256, fake(2), 256, fake(3), fake(4), 100, 100, None,
+                                   None) == moss.MOSS_EINVAL  # gate stride below n
+    assert L.moss_k_gemm_gated_add(100, 256, 256, fake(1), 256, fake(2), 256, fake(3), fake(4), 1536, 100,
+                                   fake(3, 256), None) == moss.MOSS_EALIAS  # out inside h
 
 
 def test_probe_arguments():

@@ -132,6 +132,50 @@ def test_gemm_strided():
     assert np.all(got[:, n:] == 0)
 
 
+@pytest.mark.parametrize("m,f,k", [(72, 1024, 256), (1058, 384, 512), (4130, 12288, 3072)])
+def test_gemm_silu(m, f, k):
+    """The up projection with the SiLU gate in its epilogue (a9 + a10 as the block runs them)."""
+    G.say(f"gemm_silu M={m} F={f} K={k}")
+    a = synth.make_tensor(12, 0, (m, k))
+    w = synth.make_tensor(12, 1, (2 * f, k), std=0.02)
+    z = G.empty_bf16(m, f)
+    moss.moss_k_gemm_silu(m, f, k, G.dev(a), k, G.dev(w), k, z, f)
+    G.sync()
+    rows = np.arange(m) if m * f <= 4_000_000 else np.unique(np.r_[0:64, m - 64:m, np.linspace(0, m - 1, 150).astype(int)])
+    ref = ob.silu_gate(ob.widen_bf16(a[rows]) @ ob.widen_bf16(w).T, f)
+    # one bf16 rounding of fp32 sums of K terms and an fp32 SiLU product
+    G.assert_ulps("z", G.host_f64(z)[rows], ref, ulps=1.0, abs_floor=1e-5 * np.sqrt(k / 256))
+
+
+@pytest.mark.parametrize("batch,rows,n,k", [(1, 72, 256, 256), (2, 530, 384, 512), (2, 4130, 3072, 12288)])
+@pytest.mark.parametrize("to_bf16", [False, True])
+def test_gemm_gated_add(batch, rows, n, k, to_bf16):
+    """The out / down projection with the gated residual add in its epilogue (a6 + a7, a11 + a12)."""
+    m = batch * rows
+    G.say(f"gemm_gated_add B={batch} rows={rows} N={n} K={k} bf16 out={to_bf16}")
+    a = synth.make_tensor(13, 0, (m, k), std=0.6)
+    w = synth.make_tensor(13, 1, (n, k), std=0.02)
+    h = synth.normal_f32(13, (0, 62), (m, n), 1.0)
+    gate = ob.widen_bf16(synth.make_tensor(13, 2, (batch, 6 * n), std=0.7)).astype(np.float32)
+    hd, gd = G.dev_f32(h), G.dev_f32(gate)
+    out = G.empty_bf16(m, n) if to_bf16 else None
+    moss.moss_k_gemm_gated_add(m, n, k, G.dev(a), k, G.dev(w), k, hd, gd[:, 5 * n:], 6 * n, rows, out)
+    G.sync()
+    sel = np.arange(m) if m * n <= 4_000_000 else np.unique(np.r_[0:64, m - 64:m, np.linspace(0, m - 1, 150).astype(int)])
+    y = ob.widen_bf16(a[sel]) @ ob.widen_bf16(w).T
+    g = gate.astype(np.float64)[sel // rows, 5 * n:6 * n]
+    ref = ob.gated_add(h[sel].astype(np.float64), g, y)
+    if to_bf16:
+        G.assert_ulps("out", G.host_f64(out)[sel], ref, ulps=1.0, abs_floor=1e-5)
+        np.testing.assert_array_equal(hd.cpu().numpy(), h)
+    else:
+        got = hd.cpu().numpy().astype(np.float64)[sel]
+        # fp32 sums of K terms (bounded by 1e-6 of the sum of |terms|) plus the fp32 add
+        scale = np.abs(ob.widen_bf16(a[sel])) @ np.abs(ob.widen_bf16(w)).T
+        bound = 1e-6 * np.abs(g) * scale + 2.0 ** -22 * np.abs(ref) + 1e-30
+        assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) / bound))
+
+
 # ---- a4 q/k norm + rotary + pack --------------------------------------------------------------------
 
 @pytest.mark.parametrize("batch,n_txt,gh,gw,heads", [(1, 8, 8, 8, 2), (2, 34, 8, 12, 3), (1, 63, 11, 15, 2)])
