@@ -1,16 +1,26 @@
 """Benchmark: DiT denoiser block forwards per second at 4096 image + 34 text rows.
 
 One step is one ``moss_block_forward`` (every step of the block: row join,
-adaLN GEMV, two modulated RMSNorms, QKV / out / up / down projections, q/k
-norm + rotary pack, attention, SiLU product, two gated adds) on one batch of
-seeded synthetic inputs already resident in HBM: D = 3072, 24 heads x 128,
-MLP 12288, a 64x64 image grid plus 34 text rows (the 1024x1024 picture's
-shape on the MOSS-Image transformer page, "Measured"), weights N(0, 0.02).
+adaLN GEMV, two modulated RMSNorms, QKV projection, q/k norm + rotary pack,
+attention, out projection with the first gated residual add in its epilogue,
+up projection with the SiLU gate in its epilogue, down projection with the
+second gated residual add in its epilogue) on one batch of seeded synthetic
+inputs already resident in HBM: D = 3072, 24 heads x 128, MLP 12288, a 64x64
+image grid plus 34 text rows (the 1024x1024 picture's shape on the
+MOSS-Image transformer page, "Measured"), weights N(0, 0.02).
 
 Prints one JSON line.  ``roofline`` is for the up projection (the largest
 kernel, 43% of the block's flops), timed live with HIP events recorded by the
-library around each of its launches inside the timed region.  ``cpu_baseline``
-times the float64 oracle on one block forward of the same workload.
+library around each of its launches inside the timed region.  Its ``traffic``
+(HBM bytes per launch) comes from the committed FETCH_SIZE / WRITE_SIZE
+counter summary under ``profiles/`` when that summary was taken on the GEMM
+source as it is now, else it is null.  ``cpu_baseline`` times the float64
+oracle on one block forward of the same workload.
+
+Counter runs: ``--copy-calibration`` adds one plain 256 MiB device copy before
+the warm-up, so that each ``rocprofv3 --pmc`` run also records what the
+counter reads for a known byte count.  ``--traffic-summary FETCH_DIR
+WRITE_DIR`` (no GPU) turns the two runs' counter CSVs into the summary file.
 """
 from __future__ import annotations
 
@@ -28,6 +38,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+CALIB_BYTES = 256 << 20  # the plain device copy the counters are scaled by
+UP_KERNEL = "gemm_nt_kernel<256, 256, 2, 4, 1>"  # the up projection with the SiLU gate epilogue
+GEMM_SOURCES = ("diffusion_transformer_denoiser_amd/csrc/gemm.hip", "diffusion_transformer_denoiser_amd/csrc/common.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_up_c2_traffic.md")
 METRIC = "denoiser block-forwards/s and TFLOP/s at 4096+34 tokens; MFMA % of peak"
 
 
@@ -38,7 +52,130 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run one plain 256 MiB device copy before the warm-up (for counter runs)")
+    p.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="write the HBM traffic summary from two rocprofv3 --pmc CSV runs, then exit")
     return p.parse_args()
+
+
+def gemm_source_digest():
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per up-projection launch from the committed counter summary,
+    or None when the GEMM source differs from the one the counters were taken on."""
+    import re
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("gemm_source_sha256") != gemm_source_digest():
+        return None
+    return rec
+
+
+def read_counter_csv(folder, counter):
+    """(kernel name, grid size, value) per dispatch of one counter from a rocprofv3 CSV run."""
+    import csv
+    import glob
+    paths = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if len(paths) != 1:
+        raise SystemExit(f"{folder}: expected one counter_collection.csv, found {len(paths)}")
+    rows = []
+    with open(paths[0]) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                rows.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
+    return rows
+
+
+def traffic_summary(fetch_dir, write_dir, geom):
+    """Scale FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the up projection by
+    what each counter reads for the plain 256 MiB copy, and write the summary."""
+    per = {}
+    for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = read_counter_csv(folder, counter)
+        up = [v for name, _, v in rows if UP_KERNEL in name]
+        copies = [v for name, _, v in rows if "copyBuffer" in name]
+        if not up or not copies:
+            raise SystemExit(f"{counter}: no up-projection dispatch or no copy dispatch in {folder}")
+        calib_kib = max(copies)  # the 256 MiB copy moves far more than any upload chunk
+        factor = CALIB_BYTES / (calib_kib * 1024.0)
+        per[counter] = dict(dispatches=len(up), avg_kib=float(np.mean(up)), min_kib=min(up), max_kib=max(up),
+                            calib_kib=calib_kib, factor=factor, bytes=float(np.mean(up)) * 1024.0 * factor)
+    m = geom.batch * geom.rows
+    alg = 2 * (m * geom.d_model + 2 * geom.mlp_inner * geom.d_model + m * geom.mlp_inner)
+    total = per["FETCH_SIZE"]["bytes"] + per["WRITE_SIZE"]["bytes"]
+    rec = {"gemm_source_sha256": gemm_source_digest(), "kernel": UP_KERNEL,
+           "fetch_bytes": round(per["FETCH_SIZE"]["bytes"]), "write_bytes": round(per["WRITE_SIZE"]["bytes"]),
+           "traffic_bytes": round(total), "algorithmic_bytes": alg}
+    lines = [
+        "# Up projection (4130 x 24576 x 3072, SiLU gate epilogue) at 4096 image + 34 text rows: HBM traffic",
+        "",
+        "Commands (on one MI355X, from the repository root; one counter per run):",
+        "",
+        "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- "
+        "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration",
+        "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- "
+        "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration",
+        "    python3 bench.py --traffic-summary gpurun_out/pmc_fetch gpurun_out/pmc_write",
+        "",
+        "Each counter is scaled by what it reads for one plain 256 MiB device copy "
+        "(`__amd_rocclr_copyBuffer`) in the same run: factor = 268435456 B / (counter KiB x 1024).",
+        "",
+        "| counter | up-projection dispatches | avg KiB | min KiB | max KiB | copy KiB | factor | bytes per launch |",
+        "|---|---|---|---|---|---|---|---|",
+    ]
+    for c, d in per.items():
+        lines.append(f"| {c} | {d['dispatches']} | {d['avg_kib']:.1f} | {d['min_kib']:.1f} | {d['max_kib']:.1f} | "
+                     f"{d['calib_kib']:.1f} | {d['factor']:.3f} | {d['bytes'] / 1e6:.1f} MB |")
+    # every kernel of the run, scaled the same way (context for the block's other steps)
+    kinds = {}
+    for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        for name, grid, v in read_counter_csv(folder, counter):
+            short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+            if short.startswith("__amd") or short.startswith("at::"):
+                continue
+            kinds.setdefault((short, grid), {}).setdefault(counter, []).append(v * 1024.0 * per[counter]["factor"])
+    lines += ["", "All of the library's kernels in the same runs (MB per dispatch, scaled):", "",
+              "| kernel | grid (threads) | dispatches | fetch MB | write MB |", "|---|---|---|---|---|"]
+    for (short, grid), d in kinds.items():
+        f = d.get("FETCH_SIZE", [float("nan")])
+        w = d.get("WRITE_SIZE", [float("nan")])
+        lines.append(f"| {short} | {grid} | {len(f)} | {np.mean(f) / 1e6:.1f} | {np.mean(w) / 1e6:.1f} |")
+    lines += [
+        "",
+        "FETCH_SIZE counts what the L2 caches fetch from beyond themselves; part of it is served by the "
+        "256 MB Infinity Cache rather than HBM, so it is an upper bound on HBM reads.  The GEMM's excess "
+        "over its algorithmic bytes is operand panels re-fetched by successive groups of concurrently "
+        "running tiles on each XCD (a 4 MB L2 holds a k-slab of each panel, not whole panels).",
+    ]
+    lines += [
+        "",
+        f"HBM traffic per launch: {total / 1e6:.1f} MB against {alg / 1e6:.1f} MB algorithmic "
+        f"(A {2 * m * geom.d_model / 1e6:.1f} MB + W {4 * geom.mlp_inner * geom.d_model / 1e6:.1f} MB read, "
+        f"z {2 * m * geom.mlp_inner / 1e6:.1f} MB written): {total / alg:.2f}x.",
+        "",
+        "The record bench.py reads (null traffic once the GEMM source hash differs):",
+        "",
+        "```json",
+        json.dumps(rec),
+        "```",
+        "",
+    ]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
 
 
 def cpu_baseline(geom, acts, wbits):
@@ -58,6 +195,10 @@ def cpu_baseline(geom, acts, wbits):
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        from diffusion_transformer_denoiser_amd import synth
+        traffic_summary(*args.traffic_summary, synth.CONFIGS["c2"])
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the block forward is "
               "measured on a single MI355X).", file=sys.stderr)
@@ -93,6 +234,13 @@ def main():
     def step():
         moss.moss_block_forward(dims, x, txt, acts["txt_len"], cond, w, rope, out, ws, stream)
 
+    if args.copy_calibration:
+        src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -120,6 +268,7 @@ def main():
     up_flops = 2.0 * m * (2 * geom.mlp_inner) * geom.d_model
     up_avg_ms = float(np.mean(up_ms)) if up_ms else float("nan")
     up_tflops = up_flops / (up_avg_ms / 1e3) / 1e12
+    traffic = stored_traffic()
 
     res = {
         "metric": METRIC,
@@ -144,7 +293,11 @@ def main():
                    "global_batch": 1, "seq_len": geom.rows, "parallelism": "single GPU"},
         "roofline": {"kernel": "up projection GEMM (4130 x 24576 x 3072)", "bound": "mfma",
                      "achieved": round(up_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(up_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(up_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic["traffic_bytes"] if traffic else None,
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "algorithmic_bytes": 2 * (m * geom.d_model + 2 * geom.mlp_inner * geom.d_model
+                                               + m * geom.mlp_inner),
                      "launches_timed": len(up_ms), "avg_launch_ms": round(up_avg_ms, 5)},
     }
     if not args.no_cpu_baseline:

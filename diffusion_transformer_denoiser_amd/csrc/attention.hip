@@ -17,7 +17,12 @@
 //  * Per key tile a wavefront computes S^T = K Q^T (keys x queries) with
 //    v_mfma_f32_32x32x16_bf16, so lane l holds 32 of the 64 scores of ONE
 //    query and lane l ^ 32 the other 32; the max and the sum need one
-//    v_permlane32_swap each.
+//    v_permlane32_swap each.  The two 32-key accumulators (and the four PV
+//    accumulators) alternate, so no MFMA waits for the result of the one
+//    before it, and fragment reads run four MFMAs ahead of their use.
+//  * The query fragments are loaded once, before the key loop, and marked
+//    ready at the first barrier, so the loop never waits on the vector memory
+//    counter (which the in-flight tile loads share) for them.
 //  * Scores are scaled into log2 units inside the exp2 argument (one FMA per
 //    score) and exponentiated with v_exp_f32 directly (results below 2^-126
 //    of the row max flush to zero, which no bf16 probability could hold).
@@ -37,6 +42,11 @@
 #include "launch.h"
 
 namespace {
+
+// V fragment reads issued ahead of the PV MFMAs (0: the compiler's own order)
+#ifndef MOSS_ATTN_SCHED
+#define MOSS_ATTN_SCHED 4
+#endif
 
 constexpr int BQ = 128;  // queries per workgroup
 constexpr int BKV = 64;  // keys per tile
@@ -126,23 +136,45 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const uint16_t* _
 
   const int n_tiles = (rows + BKV - 1) / BKV;
   issue(0);
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  // The query fragments pass through this statement, so the compiler treats
+  // them as ready here and the loop's MFMAs never wait on the vector memory
+  // counter (which the tile loads also count) for them.
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier"
+               : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]), "+v"(qf[4]), "+v"(qf[5]), "+v"(qf[6]),
+                 "+v"(qf[7])
+               :
+               : "memory");
   for (int kt = 0; kt < n_tiles; ++kt) {
     // stage (kt+1)&1 held tile kt-1, whose reads finished before the previous barrier
     if (kt + 1 < n_tiles) issue(kt + 1);
     const char* st = smem + (kt & 1) * kStage;
 
+    // S^T for keys 0-31 (h2 = 0) and 32-63 (h2 = 1): the two accumulator
+    // chains alternate so no MFMA waits on the one just issued
     f32x16 sacc[2];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[h2][e] = 0.0f;
+    bf16x8 kf[8][2];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(st + kfo[h2][s]);
-        sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[h2], 0, 0, 0);
-      }
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) kf[s][h2] = *reinterpret_cast<const bf16x8*>(st + kfo[h2][s]);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s][h2], qf[s], sacc[h2], 0, 0, 0);
+#if MOSS_ATTN_SCHED
+    // K fragment reads run 4 ahead of the MFMAs that use them
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int q = 0; q < 12; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+#endif
 
     // lane holds keys 32*h2 + 8*q + 4*hh + e at sacc[h2][4q + e]
     const int key0 = kt * BKV;
@@ -188,14 +220,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const uint16_t* _
         }
     l_run += pair_sum(lsum);
 
-    // O^T += V^T P^T over four 16-key steps
+    // O^T += V^T P^T over four 16-key steps; the four accumulators alternate
+    bf16x8 vf[4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(st + vfo[i][s]);
-        acc_o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], acc_o[i], 0, 0, 0);
-      }
+      for (int i = 0; i < 4; ++i) vf[s][i] = *reinterpret_cast<const bf16x8*>(st + vfo[i][s]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc_o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s][i], pf[s], acc_o[i], 0, 0, 0);
+#if MOSS_ATTN_SCHED
+    __builtin_amdgcn_sched_group_barrier(0x100, MOSS_ATTN_SCHED, 0);
+#pragma unroll
+    for (int q = 0; q < 16 - MOSS_ATTN_SCHED; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, MOSS_ATTN_SCHED, 0);
+#endif
 
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   }

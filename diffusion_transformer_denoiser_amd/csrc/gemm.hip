@@ -17,9 +17,14 @@
 //  * A slab row is 64 bytes (32 bf16 of k).  The 16-byte chunk c of row r is
 //    stored at c ^ ((r >> 2) & 3), so the 16 rows a 16-lane group reads for
 //    one operand fragment land in 16 distinct 16-byte slots of the LDS banks.
-//  * Tiles are numbered M-fastest and grouped per XCD: workgroup ids are
-//    dealt round-robin over the 8 XCDs, so consecutive ids are remapped to
-//    give each XCD a contiguous run of tiles that share weight slabs in its L2.
+//  * Within a k-step the wavefront issues the next k-step's fragment reads
+//    one after each of its first MFMAs (a scheduling-group constraint), so the
+//    reads have most of the step's MFMAs to land.
+//  * Tiles are numbered in groups of six column tiles, row-major within a
+//    group, and workgroup ids (dealt round-robin over the 8 XCDs) are
+//    remapped so each XCD runs a contiguous stretch of that order: the ~32
+//    tiles an XCD holds at once span about 5 row and 6 column panels, which
+//    its L2 shares (fetch from beyond L2 down ~40% from an M-fastest order).
 //  * The weight tile is the MFMA's first operand and the activation tile the
 //    second, so a lane's accumulators hold runs of four consecutive output
 //    columns of one row and leave in 8-byte stores.
@@ -53,13 +58,42 @@ struct EpiArgs {
   uint16_t* out16;    // kGatedAdd: when set, bf16 result here instead of updating h
 };
 
-// Workgroup id -> (tile_m, tile_n), M fastest, a contiguous run of tiles per XCD.
-__device__ __forceinline__ void tile_of(int id, int nblk, int mt, int& tm, int& tn) {
+#ifndef MOSS_GEMM_GROUP
+#define MOSS_GEMM_GROUP 6
+#endif
+constexpr int kGroupN = MOSS_GEMM_GROUP;
+// LDS fragment reads placed after each MFMA of the other k-step (0: the compiler's own order)
+#ifndef MOSS_GEMM_SCHED
+#define MOSS_GEMM_SCHED 1
+#endif  // column tiles per group
+
+// Workgroup id -> (tile_m, tile_n).  Logical order: column tiles in groups of
+// kGroupN, each group row-major (N fastest); workgroup ids are dealt
+// round-robin over the 8 XCDs, so they are remapped to give each XCD a
+// contiguous run of that order.
+__device__ __forceinline__ void tile_of(int id, int mt, int nt, int& tm, int& tn) {
+  const int nblk = mt * nt;
   const int per = nblk / 8, rem = nblk % 8;
   const int x = id % 8, l = id / 8;
   const int logical = (x < rem) ? x * (per + 1) + l : rem * (per + 1) + (x - rem) * per + l;
-  tm = logical % mt;
-  tn = logical / mt;
+  const int g = logical / (kGroupN * mt), r = logical % (kGroupN * mt);
+  const int cols = min(kGroupN, nt - g * kGroupN);
+  tm = r / cols;
+  tn = g * kGroupN + r % cols;
+}
+
+// Instruction order for one k-step: one MFMA, then RPM LDS reads, repeated
+// until the NR reads are placed, then the remaining MFMAs, so the last read
+// still has several MFMAs behind it before its data are needed.
+template <int RPM, int NR, int NMFMA>
+__device__ __forceinline__ void sched_interleave() {
+  if constexpr (NR > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NR < RPM ? NR : RPM, 0);
+    sched_interleave<RPM, (NR > RPM ? NR - RPM : 0), NMFMA - 1>();
+  } else {
+    __builtin_amdgcn_sched_group_barrier(0x008, NMFMA, 0);
+  }
 }
 
 template <int BM, int BN, int WM, int WN, int EPI>
@@ -74,12 +108,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
   constexpr int LA = AB / 1024 / NW, LB = BB / 1024 / NW;    // 1 KiB load instructions per wavefront
   constexpr int PER = LA + LB;
   static_assert(LA * NW * 1024 == AB && LB * NW * 1024 == BB, "slab / wavefront mismatch");
-  static_assert(EPI != kSiluGate || FN == 2, "the SiLU epilogue pairs a gate and an up fragment per wavefront");
+  static_assert(EPI != kSiluGate || FN % 2 == 0, "the SiLU epilogue pairs gate and up fragments per wavefront");
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * (AB + BB)];
 
   const int mt = (m + BM - 1) / BM;
   int tm, tn;
-  tile_of(blockIdx.x, mt * (n / BN), mt, tm, tn);
+  tile_of(blockIdx.x, mt, n / BN, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
   const int wm = wave / WN, wn = wave % WN;
@@ -99,9 +133,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
     const int r = (wave + NW * i) * 16 + (lane >> 2);
     int wrow = n0 + r;
     if (EPI == kSiluGate) {
-      // tile row r -> wavefront r / TN, fragment (r % TN) / 32: fragment 0 = gate rows, 1 = up rows
-      const int zc = tn * (BN / 2) + (r / TN) * 32 + (r & 31);
-      wrow = ((r % TN) >= 32 ? n / 2 : 0) + zc;
+      // tile row r -> wavefront r / TN, fragment f = (r % TN) / 32: even f = gate rows, odd f = the
+      // up rows of the same outputs
+      const int f = (r % TN) / 32;
+      const int zc = tn * (BN / 2) + (r / TN) * (TN / 2) + (f / 2) * 32 + (r & 31);
+      wrow = ((f & 1) ? n / 2 : 0) + zc;
     }
     gb[i] = w + (size_t)wrow * ldw + ((lane & 3) ^ ((r >> 2) & 3)) * 8;
   }
@@ -171,6 +207,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
     for (int i = 0; i < FN; ++i)
 #pragma unroll
       for (int j = 0; j < FM; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw1[i], fa1[j], acc[i][j], 0, 0, 0);
+#if MOSS_GEMM_SCHED
+    // issue each k-step's fragment reads early in the other k-step's MFMAs
+    sched_interleave<MOSS_GEMM_SCHED, FM + FN, FM * FN>();
+    sched_interleave<MOSS_GEMM_SCHED, FM + FN, FM * FN>();
+#endif
     // slab kt+2 resident for the next iteration (only slab kt+3 may stay in flight)
     if (kt + STAGES - 1 < nk) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(PER) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
@@ -185,14 +226,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
     if (EPI == kSiluGate) {
       uint16_t* crow = c + (size_t)row * ldc;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = tn * (BN / 2) + wn * 32 + 8 * q + 4 * hh;
-        float z[4];
+      for (int pr = 0; pr < FN / 2; ++pr)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) z[e] = silu_f32(acc[0][j][4 * q + e]) * acc[1][j][4 * q + e];
-        u32x2 v = {pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
-        *reinterpret_cast<u32x2*>(crow + col) = v;
-      }
+        for (int q = 0; q < 4; ++q) {
+          const int col = tn * (BN / 2) + wn * (TN / 2) + pr * 32 + 8 * q + 4 * hh;
+          float z[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[e] = silu_f32(acc[2 * pr][j][4 * q + e]) * acc[2 * pr + 1][j][4 * q + e];
+          u32x2 v = {pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+          *reinterpret_cast<u32x2*>(crow + col) = v;
+        }
     } else if (EPI == kGatedAdd) {
       const int b = row / ep.rows_per_item;
       const float* g = ep.gate + (size_t)b * ep.gate_stride;
