@@ -16,6 +16,7 @@ import numpy as np
 from diffusion_transformer_denoiser_amd import synth
 from oracle import brute_force as bf
 from oracle import dit_block as ob
+from oracle import sampler as osm
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -359,6 +360,64 @@ def pin_rounding_mode():
     _close(ob.round_bf16(v.astype(np.float64)), ob.widen_bf16(synth.f32_to_bf16_bits(v)), 0.0)
 
 
+# ----------------------------------------------------------------------------
+# the sampler step around the stack (oracle/sampler.py)
+# ----------------------------------------------------------------------------
+
+
+def pin_guidance_hand_worked():
+    """Worked by hand: x = 1, v_pos = 2, v_neg = 0.5, g = 3, dsigma = -0.02:
+    v = 0.5 + 3 * 1.5 = 5, x' = 1 - 0.1 = 0.9; and with v_pos = -1, v_neg = 1,
+    g = 3: v = 1 + 3 * (-2) = -5, x' = 1 + 0.1 = 1.1."""
+    got = osm.guidance_euler(np.array([1.0, 1.0]), np.array([2.0, -1.0]), np.array([0.5, 1.0]), 3.0, -0.02)
+    _close(got, [0.9, 1.1], 1e-15)
+
+
+def pin_guidance_limits():
+    """g = 1 is the positive velocity alone (so the negative pass may be
+    skipped), g = 0 the negative alone; equal velocities make g irrelevant;
+    dsigma = 0 leaves x; the step is linear in dsigma."""
+    rng = np.random.default_rng(5)
+    x, vp, vn = (rng.standard_normal((7, 16)) for _ in range(3))
+    _close(osm.guidance_euler(x, vp, vn, 1.0, 0.3), x + 0.3 * vp, 1e-15)
+    _close(osm.guidance_euler(x, vp, None, 1.0, 0.3), x + 0.3 * vp, 1e-15)
+    _close(osm.guidance_euler(x, vp, vn, 0.0, 0.3), x + 0.3 * vn, 1e-15)
+    _close(osm.guidance_euler(x, vp, vp, 3.0, 0.3), osm.guidance_euler(x, vp, vp, -7.0, 0.3), 1e-14)
+    assert np.array_equal(osm.guidance_euler(x, vp, vn, 3.0, 0.0), x)
+    d1 = osm.guidance_euler(x, vp, vn, 3.0, 0.01) - x
+    d2 = osm.guidance_euler(x, vp, vn, 3.0, 0.02) - x
+    _close(d2, 2.0 * d1, 1e-13)
+    try:
+        osm.guidance(vp, None, 3.0)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("skipping the negative pass away from guidance 1 must be refused")
+
+
+def pin_skip_block():
+    """A skipped block leaves that item's residual alone: no skips is the
+    plain stack; a block skipped for every item is the stack without it; a
+    block skipped for one item changes only that item; skipping every block
+    returns the joined rows."""
+    geom = tiny_geoms()[1]
+    x, txt, txt_len, cond, ws = f64_inputs(geom, seed=3, n_blocks=3)
+    cos, sin = ob.rope_tables(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, geom.head_dim)
+    none = [[False, False]] * 3
+    full = ob.stack_forward(x, txt, txt_len, cond, ws, cos, sin, geom.eps)
+    _close(osm.stack_forward_skip(x, txt, txt_len, cond, ws, none, cos, sin, geom.eps), full, 1e-11)
+    without = ob.stack_forward(x, txt, txt_len, cond, [ws[0], ws[2]], cos, sin, geom.eps)
+    mid_all = [[False, False], [True, True], [False, False]]
+    _close(osm.stack_forward_skip(x, txt, txt_len, cond, ws, mid_all, cos, sin, geom.eps), without, 1e-11)
+    mid_one = [[False, False], [True, False], [False, False]]
+    got = osm.stack_forward_skip(x, txt, txt_len, cond, ws, mid_one, cos, sin, geom.eps)
+    _close(got[0], without[0], 1e-11)
+    _close(got[1], full[1], 1e-11)
+    every = [[True, True]] * 3
+    _close(osm.stack_forward_skip(x, txt, txt_len, cond, ws, every, cos, sin, geom.eps),
+           ob.join_rows(x, txt, txt_len), 0.0)
+
+
 ALL_PINS = [
     pin_brute_force_tiny,
     pin_brute_force_stack,
@@ -378,6 +437,9 @@ ALL_PINS = [
     pin_permutation_equivariance,
     pin_hand_worked_two_tokens,
     pin_rounding_mode,
+    pin_guidance_hand_worked,
+    pin_guidance_limits,
+    pin_skip_block,
 ]
 
 

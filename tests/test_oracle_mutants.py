@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 from oracle import dit_block as ob
+from oracle import sampler as osm
 
 from . import oracle_pins as P
 
@@ -147,6 +148,42 @@ MUTANTS = {
 }
 
 
+def _guidance_sign(v_pos, v_neg, g):
+    if v_neg is None:
+        return _orig_sampler["guidance"](v_pos, v_neg, g)
+    return np.asarray(v_pos) + g * (np.asarray(v_neg) - np.asarray(v_pos))
+
+
+def _guidance_no_base(v_pos, v_neg, g):
+    if v_neg is None:
+        return _orig_sampler["guidance"](v_pos, v_neg, g)
+    return g * (np.asarray(v_pos) - np.asarray(v_neg))
+
+
+def _euler_sign(x, v, dsigma):
+    return np.asarray(x, dtype=np.float64) - dsigma * np.asarray(v, dtype=np.float64)
+
+
+def _skip_ignored(x, txt, txt_len, cond, blocks, skip, cos, sin, eps=1e-6, rounded=False):
+    return ob.stack_forward(x, txt, txt_len, cond, blocks, cos, sin, eps, rounded)
+
+
+def _skip_other_item(x, txt, txt_len, cond, blocks, skip, cos, sin, eps=1e-6, rounded=False):
+    flipped = [list(reversed(s)) for s in skip]
+    return _orig_sampler["stack_forward_skip"](x, txt, txt_len, cond, blocks, flipped, cos, sin, eps, rounded)
+
+
+_orig_sampler = {name: getattr(osm, name) for name in ("guidance", "euler_step", "stack_forward_skip")}
+
+SAMPLER_MUTANTS = {
+    "guidance_sign": ("guidance", _guidance_sign),
+    "guidance_base_dropped": ("guidance", _guidance_no_base),
+    "euler_sign": ("euler_step", _euler_sign),
+    "skip_ignored": ("stack_forward_skip", _skip_ignored),
+    "skip_other_item": ("stack_forward_skip", _skip_other_item),
+}
+
+
 def test_unmutated_oracle_passes_every_pin():
     assert P.failing_pins() == []
 
@@ -155,4 +192,11 @@ def test_unmutated_oracle_passes_every_pin():
 def test_mutant_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
     monkeypatch.setattr(ob, attr, fn)
+    assert P.failing_pins(), f"planted mistake {name!r} passed every pin"
+
+
+@pytest.mark.parametrize("name", sorted(SAMPLER_MUTANTS))
+def test_sampler_mutant_is_caught(name, monkeypatch):
+    attr, fn = SAMPLER_MUTANTS[name]
+    monkeypatch.setattr(osm, attr, fn)
     assert P.failing_pins(), f"planted mistake {name!r} passed every pin"
