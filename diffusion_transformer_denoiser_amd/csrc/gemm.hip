@@ -40,13 +40,14 @@
 //  * kGatedAdd (the out and down projections): h[r, :] += gate[b, :] * acc on
 //    the fp32 residual, or, for the last add of a call, out = bf16(h + gate *
 //    acc) with h unchanged.  The projection output is never stored.
+#include <cmath>
+
 #include "common.h"
 #include "launch.h"
 
 namespace {
 
 constexpr int KB = 32;      // k per slab
-constexpr int STAGES = 4;   // LDS ring depth
 
 enum Epi { kStore = 0, kSiluGate = 1, kGatedAdd = 2 };
 
@@ -82,6 +83,22 @@ __device__ __forceinline__ void tile_of(int id, int mt, int nt, int& tm, int& tn
   tn = g * kGroupN + r % cols;
 }
 
+// Wait until at most `ahead` slabs of loads (PER instructions each, the
+// newest ones) are still in flight, then barrier.  vmcnt takes an immediate,
+// so each count from MAXA down has its own instruction.
+template <int PER, int MAXA>
+__device__ __forceinline__ void wait_slabs_barrier(int ahead) {
+  if constexpr (MAXA >= 1) {
+    if (ahead >= MAXA) {
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(MAXA * PER) : "memory");
+      return;
+    }
+    wait_slabs_barrier<PER, MAXA - 1>(ahead);
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+}
+
 // Instruction order for one k-step: one MFMA, then RPM LDS reads, repeated
 // until the NR reads are placed, then the remaining MFMAs, so the last read
 // still has several MFMAs behind it before its data are needed.
@@ -96,11 +113,74 @@ __device__ __forceinline__ void sched_interleave() {
   }
 }
 
+// acc[i][j] is a 32 x 32 tile of c^T: lane holds row m = l32 of c and
+// columns n = 8q + 4hh + e (e = 0..3) in acc[4q + e].
 template <int BM, int BN, int WM, int WN, int EPI>
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[BN / WN / 32][BM / WM / 32], int m0, int n0, int tn,
+                                         int wm, int wn, int l32, int hh, int m, int n, uint16_t* __restrict__ c,
+                                         int ldc, const EpiArgs& ep) {
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    const int row = m0 + wm * TM + j * 32 + l32;
+    if (row >= m) continue;
+    if (EPI == kSiluGate) {
+      uint16_t* crow = c + (size_t)row * ldc;
+#pragma unroll
+      for (int pr = 0; pr < FN / 2; ++pr)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = tn * (BN / 2) + wn * (TN / 2) + pr * 32 + 8 * q + 4 * hh;
+          float z[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[e] = silu_f32(acc[2 * pr][j][4 * q + e]) * acc[2 * pr + 1][j][4 * q + e];
+          u32x2 v = {pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+          *reinterpret_cast<u32x2*>(crow + col) = v;
+        }
+    } else if (EPI == kGatedAdd) {
+      const int b = row / ep.rows_per_item;
+      const float* g = ep.gate + (size_t)b * ep.gate_stride;
+      float* hrow = ep.h + (size_t)row * n;
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + wn * TN + i * 32 + 8 * q + 4 * hh;
+          const f32x4 g4 = *reinterpret_cast<const f32x4*>(g + col);
+          const f32x4 h4 = *reinterpret_cast<const f32x4*>(hrow + col);
+          f32x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = h4[e] + g4[e] * acc[i][j][4 * q + e];
+          if (ep.out16) {
+            u32x2 v = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+            *reinterpret_cast<u32x2*>(ep.out16 + (size_t)row * n + col) = v;
+          } else {
+            *reinterpret_cast<f32x4*>(hrow + col) = o;
+          }
+        }
+      }
+    } else {
+      uint16_t* crow = c + (size_t)row * ldc;
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + wn * TN + i * 32 + 8 * q + 4 * hh;
+          u32x2 v = {pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                     pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+          *reinterpret_cast<u32x2*>(crow + col) = v;
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, int STAGES = 4>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __restrict__ a, int lda,
                                                              const uint16_t* __restrict__ w, int ldw,
-                                                             uint16_t* __restrict__ c, int ldc, int m, int n,
-                                                             int k, EpiArgs ep) {
+                                                             uint16_t* __restrict__ c, int ldc, int m_begin,
+                                                             int m, int n, int k, EpiArgs ep) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
@@ -108,13 +188,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
   constexpr int LA = AB / 1024 / NW, LB = BB / 1024 / NW;    // 1 KiB load instructions per wavefront
   constexpr int PER = LA + LB;
   static_assert(LA * NW * 1024 == AB && LB * NW * 1024 == BB, "slab / wavefront mismatch");
+  static_assert(STAGES >= 4 && (STAGES - 3) * PER <= 63, "ring depth / vmcnt range");
   static_assert(EPI != kSiluGate || FN % 2 == 0, "the SiLU epilogue pairs gate and up fragments per wavefront");
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * (AB + BB)];
 
-  const int mt = (m + BM - 1) / BM;
+  const int mt = (m - m_begin + BM - 1) / BM;  // this launch covers rows [m_begin, m)
   int tm, tn;
   tile_of(blockIdx.x, mt, n / BN, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = m_begin + tm * BM, n0 = tn * BN;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
   const int wm = wave / WN, wn = wave % WN;
 
@@ -188,8 +269,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
   for (int p = 0; p < STAGES - 1; ++p)
     if (p < nk) issue(p);
   // slabs 0 and 1 resident before the loop (iteration 0 prefetches slab 1)
-  if (nk >= 3) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(PER) : "memory");
-  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  wait_slabs_barrier<PER, STAGES - 3>(min(nk, STAGES - 1) - 2);
 
   bf16x8 fa0[FM], fw0[FN], fa1[FM], fw1[FN];
   ldfrag(0, 0, fa0, fw0);
@@ -212,78 +292,56 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
     sched_interleave<MOSS_GEMM_SCHED, FM + FN, FM * FN>();
     sched_interleave<MOSS_GEMM_SCHED, FM + FN, FM * FN>();
 #endif
-    // slab kt+2 resident for the next iteration (only slab kt+3 may stay in flight)
-    if (kt + STAGES - 1 < nk) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(PER) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    // slab kt+2 resident for the next iteration (the slabs issued after it may stay in flight)
+    wait_slabs_barrier<PER, STAGES - 3>(min(nk - 1, kt + STAGES - 1) - (kt + 2));
   }
 
-  // acc[i][j] is a 32 x 32 tile of c^T: lane holds row m = l32 of c and
-  // columns n = 8q + 4hh + e (e = 0..3) in acc[4q + e].
-#pragma unroll
-  for (int j = 0; j < FM; ++j) {
-    const int row = m0 + wm * TM + j * 32 + l32;
-    if (row >= m) continue;
-    if (EPI == kSiluGate) {
-      uint16_t* crow = c + (size_t)row * ldc;
-#pragma unroll
-      for (int pr = 0; pr < FN / 2; ++pr)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = tn * (BN / 2) + wn * (TN / 2) + pr * 32 + 8 * q + 4 * hh;
-          float z[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) z[e] = silu_f32(acc[2 * pr][j][4 * q + e]) * acc[2 * pr + 1][j][4 * q + e];
-          u32x2 v = {pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
-          *reinterpret_cast<u32x2*>(crow + col) = v;
-        }
-    } else if (EPI == kGatedAdd) {
-      const int b = row / ep.rows_per_item;
-      const float* g = ep.gate + (size_t)b * ep.gate_stride;
-      float* hrow = ep.h + (size_t)row * n;
-#pragma unroll
-      for (int i = 0; i < FN; ++i) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = n0 + wn * TN + i * 32 + 8 * q + 4 * hh;
-          const f32x4 g4 = *reinterpret_cast<const f32x4*>(g + col);
-          const f32x4 h4 = *reinterpret_cast<const f32x4*>(hrow + col);
-          f32x4 o;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = h4[e] + g4[e] * acc[i][j][4 * q + e];
-          if (ep.out16) {
-            u32x2 v = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-            *reinterpret_cast<u32x2*>(ep.out16 + (size_t)row * n + col) = v;
-          } else {
-            *reinterpret_cast<f32x4*>(hrow + col) = o;
-          }
-        }
-      }
-    } else {
-      uint16_t* crow = c + (size_t)row * ldc;
-#pragma unroll
-      for (int i = 0; i < FN; ++i) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = n0 + wn * TN + i * 32 + 8 * q + 4 * hh;
-          u32x2 v = {pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                     pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
-          *reinterpret_cast<u32x2*>(crow + col) = v;
-        }
-      }
-    }
-  }
+  epilogue<BM, BN, WM, WN, EPI>(acc, m0, n0, tn, wm, wn, l32, hh, m, n, c, ldc, ep);
 }
 
+int cu_count() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+// Rows past the last whole 256-row tile: when that tile is mostly empty and
+// its column tiles would start one more round of 256-row tiles over the CUs,
+// the whole tiles run first and the leftover rows follow as 64- or 128-row
+// tiles (one workgroup of 4 wavefronts each).
 template <int EPI>
 hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_t* w, int ldw, uint16_t* c, int ldc,
                   const EpiArgs& ep, hipStream_t st) {
-  const int mt = (m + 255) / 256;
   if (n % 256 == 0) {
-    hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI>), dim3(mt * (n / 256)), dim3(512), 0, st, a, lda, w, ldw,
-                       c, ldc, m, n, k, ep);
+    const int nt = n / 256, full = m / 256, rem = m % 256, cus = cu_count();
+    bool split = false;
+    if (full > 0 && rem > 0 && rem <= 128) {
+      // a round of tail tiles costs about half a round of whole tiles (64 rows, measured at 4130 rows;
+      // 128 rows taken as 0.7): they are few, so each runs at its load latency
+      const double tail = rem <= 64 ? 0.55 : 0.7;
+      const double whole = std::ceil((double)full * nt / cus), all = std::ceil((double)(full + 1) * nt / cus);
+      split = whole + tail * std::ceil((double)nt / cus) < all;
+    }
+    const int m_main = split ? full * 256 : m;
+    hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI>), dim3(((m_main + 255) / 256) * nt), dim3(512), 0, st, a,
+                       lda, w, ldw, c, ldc, 0, m_main, n, k, ep);
+    if (split) {
+      if (rem <= 64)
+        hipLaunchKernelGGL((gemm_nt_kernel<64, 256, 1, 4, EPI>), dim3(nt), dim3(256), 0, st, a, lda, w, ldw, c,
+                           ldc, m_main, m, n, k, ep);
+      else
+        hipLaunchKernelGGL((gemm_nt_kernel<128, 256, 1, 4, EPI>), dim3(nt), dim3(256), 0, st, a, lda, w, ldw, c,
+                           ldc, m_main, m, n, k, ep);
+    }
   } else {
-    hipLaunchKernelGGL((gemm_nt_kernel<256, 128, 4, 2, EPI>), dim3(mt * (n / 128)), dim3(512), 0, st, a, lda, w, ldw,
-                       c, ldc, m, n, k, ep);
+    hipLaunchKernelGGL((gemm_nt_kernel<256, 128, 4, 2, EPI>), dim3(((m + 255) / 256) * (n / 128)), dim3(512), 0, st,
+                       a, lda, w, ldw, c, ldc, 0, m, n, k, ep);
   }
   return hipGetLastError();
 }

@@ -101,6 +101,10 @@ def test_mod_rmsnorm(batch, rows, d):
     (4130, 3072, 3072),  # the 4096+34-row out projection
     (513, 24576, 3072),  # the up projection's width, ragged M
     (257, 3072, 12288),  # the down projection's depth
+    # 64 column tiles: the 34 / 100 rows past the last whole 256-row tile run as a
+    # 64- / 128-row tail launch after the whole tiles (on a 256-CU device)
+    (1058, 16384, 256),
+    (1124, 16384, 256),
 ])
 def test_gemm_nt(m, n, k):
     G.say(f"gemm_nt M={m} N={n} K={k}")
@@ -132,7 +136,7 @@ def test_gemm_strided():
     assert np.all(got[:, n:] == 0)
 
 
-@pytest.mark.parametrize("m,f,k", [(72, 1024, 256), (1058, 384, 512), (4130, 12288, 3072)])
+@pytest.mark.parametrize("m,f,k", [(72, 1024, 256), (1058, 384, 512), (4130, 12288, 3072), (1124, 8192, 256)])
 def test_gemm_silu(m, f, k):
     """The up projection with the SiLU gate in its epilogue (a9 + a10 as the block runs them)."""
     G.say(f"gemm_silu M={m} F={f} K={k}")
@@ -147,7 +151,8 @@ def test_gemm_silu(m, f, k):
     G.assert_ulps("z", G.host_f64(z)[rows], ref, ulps=1.0, abs_floor=1e-5 * np.sqrt(k / 256))
 
 
-@pytest.mark.parametrize("batch,rows,n,k", [(1, 72, 256, 256), (2, 530, 384, 512), (2, 4130, 3072, 12288)])
+@pytest.mark.parametrize("batch,rows,n,k", [(1, 72, 256, 256), (2, 530, 384, 512), (2, 4130, 3072, 12288),
+                                            (2, 529, 16384, 256)])
 @pytest.mark.parametrize("to_bf16", [False, True])
 def test_gemm_gated_add(batch, rows, n, k, to_bf16):
     """The out / down projection with the gated residual add in its epilogue (a6 + a7, a11 + a12)."""
