@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void silu_cond_kernel(const uint16_t* __r
 __global__ __launch_bounds__(kThreads) void adaln_gemv_kernel(const float* __restrict__ s,
                                                               const uint16_t* __restrict__ w,
                                                               float* __restrict__ mod, int batch, int n_out,
-                                                              int d) {
+                                                              int d, unsigned skip_items) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (row >= n_out) return;
@@ -69,11 +69,15 @@ __global__ __launch_bounds__(kThreads) void adaln_gemv_kernel(const float* __res
       }
     }
   }
+  // chunks 2 and 5 are gate1 and gate2: a block skipped for an item gets zero gates there, so both
+  // gated adds leave that item's residual exactly as it was
+  const int chunk = row / d;
+  const bool gate = chunk == 2 || chunk == 5;
 #pragma unroll
   for (int b = 0; b < MOSS_MAX_BATCH; ++b) {
     if (b < batch) {
       const float t = wave_sum(acc[b]);
-      if (lane == 0) mod[(size_t)b * n_out + row] = t;
+      if (lane == 0) mod[(size_t)b * n_out + row] = (gate && ((skip_items >> b) & 1u)) ? 0.0f : t;
     }
   }
 }
@@ -179,6 +183,38 @@ __global__ __launch_bounds__(kThreads) void silu_mul_kernel(const uint16_t* __re
   }
 }
 
+// ---- the sampler step: classifier-free guidance, then one Euler step ----------------
+// x_out = x_in + dsigma * (v_neg + g * (v_pos - v_neg)); without v_neg (guidance 1)
+// x_out = x_in + dsigma * v_pos.  Eight elements per thread: one 16-byte load of
+// each velocity, two of x.
+__global__ __launch_bounds__(kThreads) void guidance_euler_kernel(const u32x4* __restrict__ v_pos,
+                                                                  const u32x4* __restrict__ v_neg, float g,
+                                                                  float dsigma, const f32x4* x_in, f32x4* x_out,
+                                                                  long total) {
+  for (long i = (long)blockIdx.x * kThreads + threadIdx.x; i < total; i += (long)gridDim.x * kThreads) {
+    float p[8], v[8];
+    unpack8(v_pos[i], p);
+    if (v_neg) {
+      float q[8];
+      unpack8(v_neg[i], q);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = q[j] + g * (p[j] - q[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = p[j];
+    }
+    const f32x4 x0 = x_in[2 * i], x1 = x_in[2 * i + 1];
+    f32x4 y0, y1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      y0[j] = x0[j] + dsigma * v[j];
+      y1[j] = x1[j] + dsigma * v[4 + j];
+    }
+    x_out[2 * i] = y0;
+    x_out[2 * i + 1] = y1;
+  }
+}
+
 // ---- rotary tables ------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void rope_build_kernel(int n_txt, int grid_w, double theta, float* rope,
                                                               int rows) {
@@ -219,10 +255,11 @@ hipError_t launch_silu_cond(const uint16_t* cond, float* s, int batch, int d, hi
   return hipGetLastError();
 }
 
-hipError_t launch_adaln_gemv(const float* s, const uint16_t* w_mod, float* mod, int batch, int d, hipStream_t st) {
+hipError_t launch_adaln_gemv(const float* s, const uint16_t* w_mod, float* mod, int batch, int d, unsigned skip_items,
+                             hipStream_t st) {
   const int n_out = 6 * d;
   hipLaunchKernelGGL(adaln_gemv_kernel, dim3((n_out + 3) / 4), dim3(kThreads), 0, st, s, w_mod, mod, batch,
-                     n_out, d);
+                     n_out, d, skip_items);
   return hipGetLastError();
 }
 
@@ -263,5 +300,14 @@ hipError_t launch_rope_build(int n_txt, int grid_h, int grid_w, float theta, flo
   const int rows = n_txt + grid_h * grid_w;
   hipLaunchKernelGGL(rope_build_kernel, dim3((rows * 64 + kThreads - 1) / kThreads), dim3(kThreads), 0, st, n_txt,
                      grid_w, (double)theta, rope, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_guidance_euler(int rows, int width, const uint16_t* v_pos, const uint16_t* v_neg, float g,
+                                 float dsigma, const float* x_in, float* x_out, hipStream_t st) {
+  const long total = (long)rows * (width / 8);
+  hipLaunchKernelGGL(guidance_euler_kernel, dim3(grid_for(total, kThreads)), dim3(kThreads), 0, st,
+                     reinterpret_cast<const u32x4*>(v_pos), reinterpret_cast<const u32x4*>(v_neg), g, dsigma,
+                     reinterpret_cast<const f32x4*>(x_in), reinterpret_cast<f32x4*>(x_out), total);
   return hipGetLastError();
 }

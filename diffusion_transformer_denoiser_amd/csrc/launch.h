@@ -10,7 +10,9 @@ struct ItemLens;
 hipError_t launch_join_rows(const uint16_t* x, const uint16_t* txt, const ItemLens& lens, float* out, int batch,
                             int n_txt, int n_img, int d, hipStream_t st);
 hipError_t launch_silu_cond(const uint16_t* cond, float* s, int batch, int d, hipStream_t st);
-hipError_t launch_adaln_gemv(const float* s, const uint16_t* w_mod, float* mod, int batch, int d, hipStream_t st);
+// mod = W_mod s per item; items whose bit is set in skip_items get zero gate1 and gate2.
+hipError_t launch_adaln_gemv(const float* s, const uint16_t* w_mod, float* mod, int batch, int d, unsigned skip_items,
+                             hipStream_t st);
 hipError_t launch_mod_rmsnorm(const float* h, const float* shift, const float* scale, int mod_stride,
                               uint16_t* out, int batch, int rows, int d, float eps, hipStream_t st);
 // h (fp32) + gate * y: in place when out16 is null, else into out16 (bf16) with h unchanged.
@@ -18,6 +20,9 @@ hipError_t launch_gated_add(float* h, const float* gate, int gate_stride, const 
                             int batch, int rows, int d, hipStream_t st);
 hipError_t launch_silu_mul(const uint16_t* u, uint16_t* z, int rows, int f, hipStream_t st);
 hipError_t launch_rope_build(int n_txt, int grid_h, int grid_w, float theta, float* rope, hipStream_t st);
+// x_out = x_in + dsigma * (v_neg + g (v_pos - v_neg)), or x_in + dsigma * v_pos without v_neg; width % 8 == 0.
+hipError_t launch_guidance_euler(int rows, int width, const uint16_t* v_pos, const uint16_t* v_neg, float g,
+                                 float dsigma, const float* x_in, float* x_out, hipStream_t st);
 
 // c[m, n] = sum_k a[m, k] w[n, k]; n % 128 == 0, k % 64 == 0, strides % 8 == 0.
 hipError_t launch_gemm_nt(int m, int n, int k, const uint16_t* a, int lda, const uint16_t* w, int ldw,

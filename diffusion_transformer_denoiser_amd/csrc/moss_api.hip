@@ -174,7 +174,9 @@ struct Ctx {
 
 // One block on the fp32 residual h; when out16 is not null the block's last
 // gated add writes the bf16 result there instead of updating h.
-int run_block(const Ctx& c, const moss_block_weights* w, const float* rope, float* h, uint16_t* out16) {
+// Items whose bit is set in skip_items get zero gates, so the block leaves their residual unchanged.
+int run_block(const Ctx& c, const moss_block_weights* w, const float* rope, float* h, uint16_t* out16,
+              unsigned skip_items) {
   const moss_dims* d = c.d;
   const int B = d->batch, T = d->n_txt + d->n_img, D = d->d_model, F = d->mlp_inner, H = d->n_heads;
   const int R = B * T;
@@ -190,7 +192,7 @@ int run_block(const Ctx& c, const moss_block_weights* w, const float* rope, floa
   hipStream_t st = c.st;
   {
     StepTimer t(MOSS_STEP_ADALN, st);
-    MOSS_TRY(launch_adaln_gemv(s, w->w_mod, mod, B, D, st), "adaln_gemv");
+    MOSS_TRY(launch_adaln_gemv(s, w->w_mod, mod, B, D, skip_items, st), "adaln_gemv");
   }
   {
     StepTimer t(MOSS_STEP_NORM1, st);
@@ -271,9 +273,10 @@ int validate_forward(const moss_dims* d, int n_blocks, const uint16_t* x, const 
   return MOSS_OK;
 }
 
+// skip: null, or host [n_blocks][batch], nonzero where block i is not applied to item b.
 int forward(const moss_dims* d, int n_blocks, const uint16_t* x, const uint16_t* txt, const int32_t* txt_len,
             const uint16_t* cond, const moss_block_weights* blocks, const float* rope, uint16_t* out,
-            void* workspace, size_t ws_bytes, hipStream_t st) {
+            void* workspace, size_t ws_bytes, hipStream_t st, const uint8_t* skip = nullptr) {
   Ctx c;
   int rc = validate_forward(d, n_blocks, x, txt, txt_len, cond, blocks, rope, out, workspace, ws_bytes, &c);
   if (rc != MOSS_OK) return rc;
@@ -288,7 +291,11 @@ int forward(const moss_dims* d, int n_blocks, const uint16_t* x, const uint16_t*
   MOSS_TRY(launch_silu_cond(cond, reinterpret_cast<float*>(c.ws + c.L.s_cond), d->batch, d->d_model, st),
            "silu_cond");
   for (int i = 0; i < n_blocks; ++i) {
-    rc = run_block(c, &blocks[i], rope, h, i + 1 == n_blocks ? out : nullptr);
+    unsigned mask = 0;
+    if (skip)
+      for (int b = 0; b < d->batch; ++b)
+        if (skip[(size_t)i * d->batch + b]) mask |= 1u << b;
+    rc = run_block(c, &blocks[i], rope, h, i + 1 == n_blocks ? out : nullptr, mask);
     if (rc != MOSS_OK) return rc;
   }
   return MOSS_OK;
@@ -346,6 +353,31 @@ int moss_stack_forward(const moss_dims* dims, int32_t n_blocks, const uint16_t* 
   return forward(dims, n_blocks, x, txt, txt_len, cond, blocks, rope, out, workspace, ws_bytes, stream);
 }
 
+int moss_stack_forward_skip(const moss_dims* dims, int32_t n_blocks, const uint16_t* x, const uint16_t* txt,
+                            const int32_t* txt_len, const uint16_t* cond, const moss_block_weights* blocks,
+                            const uint8_t* skip, const float* rope, uint16_t* out, void* workspace,
+                            size_t ws_bytes, hipStream_t stream) {
+  return forward(dims, n_blocks, x, txt, txt_len, cond, blocks, rope, out, workspace, ws_bytes, stream, skip);
+}
+
+int moss_guidance_euler(int32_t rows, int32_t width, const uint16_t* v_pos, const uint16_t* v_neg, float guidance,
+                        float dsigma, const float* x_in, float* x_out, hipStream_t stream) {
+  if (rows < 0 || width < 8 || width % 8 || (long)rows * width > (1L << 31)) return MOSS_EINVAL;
+  if (!isfinite(guidance) || !isfinite(dsigma)) return MOSS_EINVAL;
+  if (!v_neg && guidance != 1.0f) return MOSS_EINVAL;  // only guidance 1 may skip the negative pass
+  if (!v_pos || !x_in || !x_out || !aligned16(v_pos) || !aligned16(x_in) || !aligned16(x_out)) return MOSS_EINVAL;
+  if (v_neg && !aligned16(v_neg)) return MOSS_EINVAL;
+  const size_t vb = 2 * (size_t)rows * width, xb = 4 * (size_t)rows * width;
+  if (overlaps(x_out, xb, v_pos, vb) || overlaps(x_out, xb, v_neg, vb)) return MOSS_EALIAS;
+  if (x_out != x_in && overlaps(x_out, xb, x_in, xb)) return MOSS_EALIAS;  // in place, or apart
+  if (rows == 0) return MOSS_OK;
+  const int rc = single_device_check();
+  if (rc != MOSS_OK) return rc;
+  MOSS_TRY(launch_guidance_euler(rows, width, v_pos, v_neg, guidance, dsigma, x_in, x_out, stream),
+           "guidance_euler");
+  return MOSS_OK;
+}
+
 int moss_k_join_rows(int32_t batch, int32_t n_txt, int32_t n_img, int32_t d_model, const uint16_t* x,
                      const uint16_t* txt, const int32_t* txt_len, float* out, hipStream_t stream) {
   moss_dims d = {batch, n_img, n_txt, d_model, d_model / MOSS_HEAD_DIM, MOSS_HEAD_DIM, 128, 1e-6f};
@@ -374,7 +406,7 @@ int moss_k_adaln_gemv(int32_t batch, int32_t d_model, const uint16_t* cond, cons
   if (rc != MOSS_OK) return rc;
   float* s = static_cast<float*>(workspace);
   MOSS_TRY(launch_silu_cond(cond, s, batch, d_model, stream), "silu_cond");
-  MOSS_TRY(launch_adaln_gemv(s, w_mod, mod, batch, d_model, stream), "adaln_gemv");
+  MOSS_TRY(launch_adaln_gemv(s, w_mod, mod, batch, d_model, 0u, stream), "adaln_gemv");
   return MOSS_OK;
 }
 

@@ -52,6 +52,10 @@ _SIGS = {
                                           ctypes.POINTER(moss_block_weights), c_vp, c_vp, c_vp, c_size, c_vp]),
     "moss_stack_forward": (ctypes.c_int, [ctypes.POINTER(moss_dims), c_i32, c_vp, c_vp, c_vp, c_vp,
                                           ctypes.POINTER(moss_block_weights), c_vp, c_vp, c_vp, c_size, c_vp]),
+    "moss_stack_forward_skip": (ctypes.c_int, [ctypes.POINTER(moss_dims), c_i32, c_vp, c_vp, c_vp, c_vp,
+                                               ctypes.POINTER(moss_block_weights), c_vp, c_vp, c_vp, c_vp, c_size,
+                                               c_vp]),
+    "moss_guidance_euler": (ctypes.c_int, [c_i32, c_i32, c_vp, c_vp, c_f32, c_f32, c_vp, c_vp, c_vp]),
     "moss_k_join_rows": (ctypes.c_int, [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moss_k_adaln_gemv": (ctypes.c_int, [c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "moss_k_mod_rmsnorm": (ctypes.c_int, [c_i32, c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp]),
@@ -178,6 +182,28 @@ def moss_stack_forward(dims, blocks, x, txt, txt_len, cond, rope, out, workspace
                                   workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                   _s(stream))
     _check(rc, "moss_stack_forward")
+
+
+def moss_stack_forward_skip(dims, blocks, skip, x, txt, txt_len, cond, rope, out, workspace, stream=None) -> None:
+    """``skip``: None, or n_blocks rows of batch flags (true = block not applied to that item)."""
+    arr = (moss_block_weights * len(blocks))(
+        *[b if isinstance(b, moss_block_weights) else make_weights(b) for b in blocks])
+    sk = None
+    if skip is not None:
+        flat = [1 if f else 0 for row in skip for f in row]
+        flags = (ctypes.c_uint8 * len(flat))(*flat)  # alive until the call returns
+        sk = ctypes.cast(flags, c_vp)
+    rc = lib().moss_stack_forward_skip(ctypes.byref(dims), len(blocks), _p(x), _p(txt),
+                                       ctypes.cast(_lens(txt_len), c_vp), _p(cond), arr, sk, _p(rope), _p(out),
+                                       _p(workspace),
+                                       workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                       _s(stream))
+    _check(rc, "moss_stack_forward_skip")
+
+
+def moss_guidance_euler(rows, width, v_pos, v_neg, guidance, dsigma, x_in, x_out, stream=None) -> None:
+    _check(lib().moss_guidance_euler(rows, width, _p(v_pos), _p(v_neg), guidance, dsigma, _p(x_in), _p(x_out),
+                                     _s(stream)), "moss_guidance_euler")
 
 
 def moss_k_join_rows(batch, n_txt, n_img, d_model, x, txt, txt_len, out, stream=None) -> None:

@@ -140,6 +140,36 @@ int moss_stack_forward(const moss_dims* dims, int32_t n_blocks, const uint16_t* 
                        const float* rope, uint16_t* out, void* workspace, size_t ws_bytes,
                        hipStream_t stream);
 
+/* moss_stack_forward with some blocks not applied to some items: skip is a
+ * host array [n_blocks][batch] (row i for block i); a nonzero skip[i][b]
+ * leaves item b's residual unchanged through block i while the other items
+ * run it (the CUDA port page's guidance pass skips one block on one branch,
+ * TensorFold PR #2281, "What this changes").  Implemented by zeroing that
+ * item's two gates for that block, so its residual passes through exactly;
+ * the block's compute is still spent on the item.  skip == NULL is
+ * moss_stack_forward.  Other arguments, ownership and errors as
+ * moss_stack_forward. */
+int moss_stack_forward_skip(const moss_dims* dims, int32_t n_blocks, const uint16_t* x, const uint16_t* txt,
+                            const int32_t* txt_len, const uint16_t* cond, const moss_block_weights* blocks,
+                            const uint8_t* skip, const float* rope, uint16_t* out, void* workspace,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* One sampler step on a latent (the CUDA port page, TensorFold PR #2281,
+ * "What this changes": classifier-free guidance with an empty negative, and
+ * guidance 1 skipping the negative pass; the transformer page, "Measured":
+ * Euler steps at guidance 3):
+ *   x_out = x_in + dsigma * (v_neg + guidance * (v_pos - v_neg)),
+ * or x_out = x_in + dsigma * v_pos when v_neg is NULL (guidance must then be
+ * 1).  v_pos, v_neg: [rows, width] bf16 velocities (device); x_in, x_out:
+ * [rows, width] fp32 latents (device; x_out == x_in updates in place, any
+ * other overlap is refused).  dsigma = sigma_next - sigma_now.  Arithmetic in
+ * fp32.  width % 8 == 0, pointers 16-byte aligned.  MOSS_EINVAL on bad sizes,
+ * pointers or non-finite guidance/dsigma, or a NULL v_neg with guidance != 1;
+ * MOSS_EALIAS when x_out overlaps a velocity or partly overlaps x_in.
+ * rows == 0 is a no-op. */
+int moss_guidance_euler(int32_t rows, int32_t width, const uint16_t* v_pos, const uint16_t* v_neg, float guidance,
+                        float dsigma, const float* x_in, float* x_out, hipStream_t stream);
+
 /* ---- single-step entry points (same conventions; used by the tests) ----- */
 
 /* Packed attention layouts written by moss_k_qk_norm_rope_pack and read by

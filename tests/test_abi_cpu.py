@@ -180,3 +180,40 @@ def test_probe_arguments():
     assert L.moss_probe_arm(13, 4) == moss.MOSS_EINVAL
     assert L.moss_probe_arm(3, 0) == moss.MOSS_EINVAL
     assert L.moss_probe_collect(None, -1) == -moss.MOSS_EINVAL
+
+
+def test_guidance_euler_validates():
+    L = moss.lib()
+    ok = (fake(1), fake(2), 3.0, -0.02, fake(3), fake(4), None)
+    assert L.moss_guidance_euler(10, 12, *ok) == moss.MOSS_EINVAL  # width % 8
+    assert L.moss_guidance_euler(-1, 16, *ok) == moss.MOSS_EINVAL
+    assert L.moss_guidance_euler(10, 16, fake(1), None, 3.0, -0.02, fake(3), fake(4), None) == moss.MOSS_EINVAL
+    assert L.moss_guidance_euler(10, 16, fake(1), fake(2), float("nan"), -0.02, fake(3), fake(4), None) == \
+        moss.MOSS_EINVAL
+    assert L.moss_guidance_euler(10, 16, fake(1), fake(2), 3.0, float("inf"), fake(3), fake(4), None) == \
+        moss.MOSS_EINVAL
+    assert L.moss_guidance_euler(10, 16, fake(1, 8), fake(2), 3.0, -0.02, fake(3), fake(4), None) == moss.MOSS_EINVAL
+    assert L.moss_guidance_euler(10, 16, fake(1), fake(2), 3.0, -0.02, fake(3), fake(1, 64), None) == \
+        moss.MOSS_EALIAS  # x_out over v_pos
+    assert L.moss_guidance_euler(10, 16, fake(1), fake(2), 3.0, -0.02, fake(3), fake(3, 32), None) == \
+        moss.MOSS_EALIAS  # x_out partly over x_in
+    assert L.moss_guidance_euler(0, 16, *ok) == moss.MOSS_OK  # nothing to do, no device needed
+    if moss.moss_device_check(0) != moss.MOSS_OK:
+        assert L.moss_guidance_euler(10, 16, *ok) == moss.MOSS_EDEVICE
+        assert L.moss_guidance_euler(10, 16, fake(1), None, 1.0, -0.02, fake(3), fake(3), None) == \
+            moss.MOSS_EDEVICE  # guidance 1 without the negative pass, in place
+
+
+def test_stack_skip_validates():
+    L = moss.lib()
+    d = c2_dims()
+    flags = (ctypes.c_uint8 * 2)(0, 1)
+    rc = L.moss_stack_forward_skip(ctypes.byref(d), 0, fake(1), fake(2), None, fake(3), ctypes.byref(weights()),
+                                   ctypes.cast(flags, ctypes.c_void_p), fake(4), fake(5), fake(6),
+                                   moss.moss_workspace_bytes(d, 1), None)
+    assert rc == moss.MOSS_EINVAL
+    if moss.moss_device_check(0) != moss.MOSS_OK:
+        rc = L.moss_stack_forward_skip(ctypes.byref(d), 1, fake(1), fake(2), None, fake(3), ctypes.byref(weights()),
+                                       ctypes.cast(flags, ctypes.c_void_p), fake(4), fake(5), fake(6),
+                                       moss.moss_workspace_bytes(d, 1), None)
+        assert rc == moss.MOSS_EDEVICE

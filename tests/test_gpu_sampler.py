@@ -1,0 +1,118 @@
+"""The sampler step around the stack against the float64 oracle (GPU): the
+guidance + Euler update of a latent, and a block skipped for one item of the
+guidance pair."""
+import numpy as np
+import pytest
+
+from diffusion_transformer_denoiser_amd import moss, synth
+from oracle import dit_block as ob
+from oracle import sampler as osm
+
+from . import gpu_util as G
+from .test_gpu_block import STRONG, check
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    t = G.torch()
+    assert t.cuda.is_available(), "no GPU visible"
+    assert moss.moss_device_check(0) == moss.MOSS_OK, "device 0 is not gfx950"
+    return t
+
+
+def _latent_case(rows, width, seed):
+    v_pos = synth.make_tensor(seed, 0, (rows, width), std=1.0)
+    v_neg = synth.make_tensor(seed, 1, (rows, width), std=1.0)
+    x = synth.normal_f32(seed, (0, 63), (rows, width), 1.0)
+    return v_pos, v_neg, x
+
+
+def _bound(x, vp, vn, g, ds):
+    """fp32 evaluation of x + ds (vn + g (vp - vn)): a few roundings of terms of this size."""
+    return 4 * 2.0 ** -24 * (np.abs(x) + abs(ds) * (np.abs(vn) + abs(g) * (np.abs(vp) + np.abs(vn)))) + 1e-30
+
+
+@pytest.mark.parametrize("rows,width,g,ds", [
+    (4096, 128, 3.0, -0.02),   # the 1024x1024 latent: 4096 rows of 128, guidance 3
+    (4125, 128, 3.0, -0.0185),  # the 1200x880 latent
+    (7, 24, -1.5, 0.25),        # ragged, negative guidance, positive step
+])
+def test_guidance_euler(rows, width, g, ds):
+    G.say(f"guidance_euler rows={rows} width={width} g={g} dsigma={ds}")
+    vp, vn, x = _latent_case(rows, width, 21)
+    xd = G.dev_f32(x)
+    out = G.empty_f32(rows, width)
+    moss.moss_guidance_euler(rows, width, G.dev(vp), G.dev(vn), g, ds, xd, out)
+    G.sync()
+    vpf, vnf = ob.widen_bf16(vp), ob.widen_bf16(vn)
+    ref = osm.guidance_euler(x.astype(np.float64), vpf, vnf, g, ds)
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= _bound(x, vpf, vnf, g, ds))
+    np.testing.assert_array_equal(xd.cpu().numpy(), x)  # the input latent is untouched
+
+
+def test_guidance_one_skips_negative_in_place():
+    rows, width = 4096, 128
+    vp, vn, x = _latent_case(rows, width, 22)
+    G.say("guidance_euler g=1 without the negative pass, in place")
+    xd = G.dev_f32(x)
+    moss.moss_guidance_euler(rows, width, G.dev(vp), None, 1.0, -0.02, xd, xd)
+    G.sync()
+    vpf = ob.widen_bf16(vp)
+    ref = osm.guidance_euler(x.astype(np.float64), vpf, None, 1.0, -0.02)
+    got = xd.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= _bound(x, vpf, vpf, 1.0, -0.02))
+
+
+def test_guidance_euler_zero_rows_is_noop():
+    # a zero-row call touches nothing (pointers are still validated)
+    out = G.empty_f32(1, 8)
+    out.fill_(7.0)
+    vp = G.empty_bf16(1, 8)
+    moss.moss_guidance_euler(0, 8, vp, vp, 3.0, 0.1, out, out)
+    G.sync()
+    assert np.all(out.cpu().numpy() == 7.0)
+
+
+def _stack_skip_gpu(geom, acts, ws, skip):
+    t = G.torch()
+    dims = G.geometry_dims(geom)
+    rope = G.empty_f32(2, geom.rows, 64)
+    moss.moss_rope_build(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, rope)
+    workspace = t.empty(moss.moss_workspace_bytes(dims, len(ws)), dtype=t.uint8, device="cuda")
+    out = G.empty_bf16(geom.batch, geom.rows, geom.d_model)
+    dev_w = [{k: G.dev(v) for k, v in w.items()} for w in ws]
+    moss.moss_stack_forward_skip(dims, dev_w, skip, G.dev(acts["x"]), G.dev(acts["txt"]), acts["txt_len"],
+                                 G.dev(acts["cond"]), rope, out, workspace)
+    G.sync()
+    return out
+
+
+def test_stack_skip_one_block_per_item():
+    """Block 1 skipped for item 0, block 2 for item 1 (c0 geometry, guidance-pair batch)."""
+    geom = synth.smaller(synth.CONFIGS["c0"], batch=2, txt_len=(8, 2))
+    G.say("stack_skip c0-strong x3")
+    acts = synth.make_activations(geom, 6)
+    ws = [synth.make_block_weights(geom, 6, i, std=STRONG) for i in range(3)]
+    skip = [[False, False], [True, False], [False, True]]
+    got = G.host_f64(_stack_skip_gpu(geom, acts, ws, skip))
+    cos, sin = ob.rope_tables(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, geom.head_dim)
+    x, txt, cond = ob.widen_bf16(acts["x"]), ob.widen_bf16(acts["txt"]), ob.widen_bf16(acts["cond"])
+    ref = osm.stack_forward_skip(x, txt, acts["txt_len"], cond, [ob.weights_f64(w) for w in ws], skip, cos, sin,
+                                 geom.eps)
+    check(geom, acts, got, ref)
+
+
+def test_stack_skip_every_block_passes_rows_through():
+    """An item that skips every block comes out as its joined input rows, bit for bit."""
+    geom = synth.smaller(synth.CONFIGS["c0"], batch=2, txt_len=(8, 5))
+    G.say("stack_skip all blocks for item 1")
+    acts = synth.make_activations(geom, 7)
+    ws = [synth.make_block_weights(geom, 7, i, std=STRONG) for i in range(2)]
+    got = _stack_skip_gpu(geom, acts, ws, [[False, True], [False, True]]).cpu().numpy().view(np.uint16)
+    n = acts["txt_len"][1]
+    np.testing.assert_array_equal(got[1, :n], acts["txt"][1, :n])
+    assert np.all(got[1, n:geom.n_txt] == 0)
+    np.testing.assert_array_equal(got[1, geom.n_txt:], acts["x"][1])
