@@ -138,7 +138,11 @@ def make_dims(batch, n_img, n_txt, d_model, mlp_inner, eps=1e-6, n_heads=None, h
 
 
 def make_weights(w: dict) -> moss_block_weights:
-    return moss_block_weights(*[_p(w[n]) for n in WEIGHT_FIELDS])
+    """The weight struct of one block; it keeps the tensors alive as long as it lives
+    (the struct holds raw device pointers)."""
+    s = moss_block_weights(*[_p(w[n]) for n in WEIGHT_FIELDS])
+    s._tensors = [w[n] for n in WEIGHT_FIELDS]
+    return s
 
 
 # ---- the entry points -------------------------------------------------------------

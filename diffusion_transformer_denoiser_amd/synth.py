@@ -93,6 +93,10 @@ CONFIGS = {
     "c3": Geometry("c3", 1, 63, 55, 75, 3072, 24, 12288),
     # 24-block stack, two guidance items: 34 and 10 valid text rows
     "c4": Geometry("c4", 2, 34, 64, 64, 3072, 24, 12288, txt_len=(34, 10), n_blocks=24),
+    # larger pictures, 16 pixels per latent row (1280x1024, 1408x1024, 1536x1024 wide x high)
+    "p1280": Geometry("p1280", 1, 34, 64, 80, 3072, 24, 12288),
+    "p1408": Geometry("p1408", 1, 34, 64, 88, 3072, 24, 12288),
+    "p1536": Geometry("p1536", 1, 34, 64, 96, 3072, 24, 12288),
 }
 
 

@@ -109,7 +109,9 @@ def test_block_sharp_logits():
     G.assert_parity("out (exact oracle)", got, oracle_forward(geom, acts, w), rel_max=5e-2)
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+# c1-c3, and the larger pictures of the CUDA port page's served-picture table
+# (5120, 5632 and 6144 image rows; the last is the one its server refused for memory)
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "p1280", "p1408", "p1536"])
 def test_block_full_size(name):
     geom = synth.CONFIGS[name]
     G.say(f"block {name}: {geom.n_txt}+{geom.n_img} rows, D={geom.d_model}")
