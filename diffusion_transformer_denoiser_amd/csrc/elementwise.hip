@@ -44,6 +44,10 @@ __global__ __launch_bounds__(kThreads) void silu_cond_kernel(const uint16_t* __r
 }
 
 // One wavefront per output row; every item of the batch shares the weight read.
+// Lane l takes the 16-byte chunks l, l + 64, ... of the row (CPL of them at
+// most) and issues all its weight loads before any arithmetic, so a
+// wavefront has its whole row in flight at once (the row is read once).
+template <int CPL>
 __global__ __launch_bounds__(kThreads) void adaln_gemv_kernel(const float* __restrict__ s,
                                                               const uint16_t* __restrict__ w,
                                                               float* __restrict__ mod, int batch, int n_out,
@@ -53,19 +57,29 @@ __global__ __launch_bounds__(kThreads) void adaln_gemv_kernel(const float* __res
   if (row >= n_out) return;
   const u32x4* wr = reinterpret_cast<const u32x4*>(w + (size_t)row * d);
   const int nch = d >> 3;
+  u32x4 wv[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+    wv[i] = c < nch ? wr[c] : u32x4{0u, 0u, 0u, 0u};
+  }
   float acc[MOSS_MAX_BATCH];
 #pragma unroll
   for (int b = 0; b < MOSS_MAX_BATCH; ++b) acc[b] = 0.0f;
-  for (int c = lane; c < nch; c += 64) {
-    float f[8];
-    unpack8(wr[c], f);
 #pragma unroll
-    for (int b = 0; b < MOSS_MAX_BATCH; ++b) {
-      if (b < batch) {
-        const f32x4* sp = reinterpret_cast<const f32x4*>(s + (size_t)b * d + 8 * c);
-        const f32x4 s0 = sp[0], s1 = sp[1];
-        acc[b] += f[0] * s0[0] + f[1] * s0[1] + f[2] * s0[2] + f[3] * s0[3] + f[4] * s1[0] +
-                  f[5] * s1[1] + f[6] * s1[2] + f[7] * s1[3];
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      float f[8];
+      unpack8(wv[i], f);
+#pragma unroll
+      for (int b = 0; b < MOSS_MAX_BATCH; ++b) {
+        if (b < batch) {
+          const f32x4* sp = reinterpret_cast<const f32x4*>(s + (size_t)b * d + 8 * c);
+          const f32x4 s0 = sp[0], s1 = sp[1];
+          acc[b] += f[0] * s0[0] + f[1] * s0[1] + f[2] * s0[2] + f[3] * s0[3] + f[4] * s1[0] +
+                    f[5] * s1[1] + f[6] * s1[2] + f[7] * s1[3];
+        }
       }
     }
   }
@@ -78,6 +92,41 @@ __global__ __launch_bounds__(kThreads) void adaln_gemv_kernel(const float* __res
     if (b < batch) {
       const float t = wave_sum(acc[b]);
       if (lane == 0) mod[(size_t)b * n_out + row] = (gate && ((skip_items >> b) & 1u)) ? 0.0f : t;
+    }
+  }
+}
+
+// The second half of a modulated RMSNorm row held by one wavefront (CPL chunks
+// of eight values per lane, ss = this lane's sum of squares): the shift and
+// scale loads go out before the cross-lane reduction they do not depend on.
+template <int CPL>
+__device__ __forceinline__ void modulate_store(const f32x4 (&v)[CPL][2], float ss, const float* __restrict__ sh,
+                                               const float* __restrict__ sc, u32x4* __restrict__ dst, int lane,
+                                               int nch, int d, float eps) {
+  f32x4 shv[CPL][2], scv[CPL][2];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      shv[i][0] = reinterpret_cast<const f32x4*>(sh + 8 * c)[0];
+      shv[i][1] = reinterpret_cast<const f32x4*>(sh + 8 * c)[1];
+      scv[i][0] = reinterpret_cast<const f32x4*>(sc + 8 * c)[0];
+      scv[i][1] = reinterpret_cast<const f32x4*>(sc + 8 * c)[1];
+    }
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      float o[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[j] = (v[i][0][j] * r) * (1.0f + scv[i][0][j]) + shv[i][0][j];
+        o[4 + j] = (v[i][1][j] * r) * (1.0f + scv[i][1][j]) + shv[i][1][j];
+      }
+      dst[c] = pack8(o);
     }
   }
 }
@@ -110,28 +159,8 @@ __global__ __launch_bounds__(kThreads) void mod_rmsnorm_kernel(const float* __re
       for (int j = 0; j < 4; ++j) ss += v[i][0][j] * v[i][0][j] + v[i][1][j] * v[i][1][j];
     }
   }
-  ss = wave_sum(ss);
-  const float r = 1.0f / sqrtf(ss / (float)d + eps);
-  const float* sh = shift + (size_t)b * mod_stride;
-  const float* sc = scale + (size_t)b * mod_stride;
-  u32x4* dst = reinterpret_cast<u32x4*>(out + (size_t)row * d);
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nch) {
-      const f32x4 sh0 = reinterpret_cast<const f32x4*>(sh + 8 * c)[0];
-      const f32x4 sh1 = reinterpret_cast<const f32x4*>(sh + 8 * c)[1];
-      const f32x4 sc0 = reinterpret_cast<const f32x4*>(sc + 8 * c)[0];
-      const f32x4 sc1 = reinterpret_cast<const f32x4*>(sc + 8 * c)[1];
-      float o[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        o[j] = (v[i][0][j] * r) * (1.0f + sc0[j]) + sh0[j];
-        o[4 + j] = (v[i][1][j] * r) * (1.0f + sc1[j]) + sh1[j];
-      }
-      dst[c] = pack8(o);
-    }
-  }
+  modulate_store<CPL>(v, ss, shift + (size_t)b * mod_stride, scale + (size_t)b * mod_stride,
+                      reinterpret_cast<u32x4*>(out + (size_t)row * d), lane, nch, d, eps);
 }
 
 // ---- a7/a12: h + gate * y on the fp32 residual ------------------------------------
@@ -164,6 +193,44 @@ __global__ __launch_bounds__(kThreads) void gated_add_kernel(f32x4* __restrict__
       h[2 * i + 1] = o1;
     }
   }
+}
+
+// ---- a0 + a2 for a call's first block: join the rows into the fp32 residual
+// and apply the first modulated RMSNorm, one wavefront per row, so h is
+// written once and not read back.  Text pad rows (r >= txt_len) are zero rows.
+template <int CPL>
+__global__ __launch_bounds__(kThreads) void join_mod_rmsnorm_kernel(
+    const u32x4* __restrict__ x, const u32x4* __restrict__ txt, ItemLens lens, const float* __restrict__ shift,
+    const float* __restrict__ scale, int mod_stride, float* __restrict__ h, uint16_t* __restrict__ out,
+    int n_txt, int n_img, int d, float eps, int total_rows) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= total_rows) return;
+  const int rows = n_txt + n_img;
+  const int b = row / rows, r = row - b * rows;
+  const int nch = d >> 3;
+  const u32x4* src = nullptr;
+  if (r >= n_txt) src = x + ((size_t)b * n_img + (r - n_txt)) * nch;
+  else if (r < lens.len[b]) src = txt + ((size_t)b * n_txt + r) * nch;
+  f32x4 v[CPL][2];
+  float ss = 0.0f;
+  f32x4* hrow = reinterpret_cast<f32x4*>(h + (size_t)row * d);
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      float f[8];
+      unpack8(src ? src[c] : u32x4{0u, 0u, 0u, 0u}, f);
+      v[i][0] = f32x4{f[0], f[1], f[2], f[3]};
+      v[i][1] = f32x4{f[4], f[5], f[6], f[7]};
+      hrow[2 * c] = v[i][0];
+      hrow[2 * c + 1] = v[i][1];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss += f[j] * f[j];
+    }
+  }
+  modulate_store<CPL>(v, ss, shift + (size_t)b * mod_stride, scale + (size_t)b * mod_stride,
+                      reinterpret_cast<u32x4*>(out + (size_t)row * d), lane, nch, d, eps);
 }
 
 // ---- a10: z = SiLU(u_gate) * u_up -------------------------------------------
@@ -258,8 +325,18 @@ hipError_t launch_silu_cond(const uint16_t* cond, float* s, int batch, int d, hi
 hipError_t launch_adaln_gemv(const float* s, const uint16_t* w_mod, float* mod, int batch, int d, unsigned skip_items,
                              hipStream_t st) {
   const int n_out = 6 * d;
-  hipLaunchKernelGGL(adaln_gemv_kernel, dim3((n_out + 3) / 4), dim3(kThreads), 0, st, s, w_mod, mod, batch,
-                     n_out, d, skip_items);
+  const int cpl = (d / 8 + 63) / 64;
+  const dim3 grid((n_out + 3) / 4), block(kThreads);
+  if (cpl <= 2)
+    hipLaunchKernelGGL(adaln_gemv_kernel<2>, grid, block, 0, st, s, w_mod, mod, batch, n_out, d, skip_items);
+  else if (cpl <= 4)
+    hipLaunchKernelGGL(adaln_gemv_kernel<4>, grid, block, 0, st, s, w_mod, mod, batch, n_out, d, skip_items);
+  else if (cpl <= 6)
+    hipLaunchKernelGGL(adaln_gemv_kernel<6>, grid, block, 0, st, s, w_mod, mod, batch, n_out, d, skip_items);
+  else if (cpl <= 8)
+    hipLaunchKernelGGL(adaln_gemv_kernel<8>, grid, block, 0, st, s, w_mod, mod, batch, n_out, d, skip_items);
+  else
+    hipLaunchKernelGGL(adaln_gemv_kernel<16>, grid, block, 0, st, s, w_mod, mod, batch, n_out, d, skip_items);
   return hipGetLastError();
 }
 
@@ -272,6 +349,8 @@ hipError_t launch_mod_rmsnorm(const float* h, const float* shift, const float* s
     hipLaunchKernelGGL(mod_rmsnorm_kernel<2>, grid, block, 0, st, h, shift, scale, mod_stride, out, total, rows, d, eps);
   else if (cpl <= 4)
     hipLaunchKernelGGL(mod_rmsnorm_kernel<4>, grid, block, 0, st, h, shift, scale, mod_stride, out, total, rows, d, eps);
+  else if (cpl <= 6)
+    hipLaunchKernelGGL(mod_rmsnorm_kernel<6>, grid, block, 0, st, h, shift, scale, mod_stride, out, total, rows, d, eps);
   else if (cpl <= 8)
     hipLaunchKernelGGL(mod_rmsnorm_kernel<8>, grid, block, 0, st, h, shift, scale, mod_stride, out, total, rows, d, eps);
   else
@@ -309,5 +388,31 @@ hipError_t launch_guidance_euler(int rows, int width, const uint16_t* v_pos, con
   hipLaunchKernelGGL(guidance_euler_kernel, dim3(grid_for(total, kThreads)), dim3(kThreads), 0, st,
                      reinterpret_cast<const u32x4*>(v_pos), reinterpret_cast<const u32x4*>(v_neg), g, dsigma,
                      reinterpret_cast<const f32x4*>(x_in), reinterpret_cast<f32x4*>(x_out), total);
+  return hipGetLastError();
+}
+
+hipError_t launch_join_mod_rmsnorm(const uint16_t* x, const uint16_t* txt, const ItemLens& lens, const float* shift,
+                                   const float* scale, int mod_stride, float* h, uint16_t* out, int batch, int n_txt,
+                                   int n_img, int d, float eps, hipStream_t st) {
+  const int total = batch * (n_txt + n_img);
+  const int cpl = (d / 8 + 63) / 64;
+  const dim3 grid((total + 3) / 4), block(kThreads);
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  const u32x4* tv = reinterpret_cast<const u32x4*>(txt);
+  if (cpl <= 2)
+    hipLaunchKernelGGL(join_mod_rmsnorm_kernel<2>, grid, block, 0, st, xv, tv, lens, shift, scale, mod_stride, h, out,
+                       n_txt, n_img, d, eps, total);
+  else if (cpl <= 4)
+    hipLaunchKernelGGL(join_mod_rmsnorm_kernel<4>, grid, block, 0, st, xv, tv, lens, shift, scale, mod_stride, h, out,
+                       n_txt, n_img, d, eps, total);
+  else if (cpl <= 6)
+    hipLaunchKernelGGL(join_mod_rmsnorm_kernel<6>, grid, block, 0, st, xv, tv, lens, shift, scale, mod_stride, h, out,
+                       n_txt, n_img, d, eps, total);
+  else if (cpl <= 8)
+    hipLaunchKernelGGL(join_mod_rmsnorm_kernel<8>, grid, block, 0, st, xv, tv, lens, shift, scale, mod_stride, h, out,
+                       n_txt, n_img, d, eps, total);
+  else
+    hipLaunchKernelGGL(join_mod_rmsnorm_kernel<16>, grid, block, 0, st, xv, tv, lens, shift, scale, mod_stride, h,
+                       out, n_txt, n_img, d, eps, total);
   return hipGetLastError();
 }

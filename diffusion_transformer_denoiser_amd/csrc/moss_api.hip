@@ -174,9 +174,15 @@ struct Ctx {
 
 // One block on the fp32 residual h; when out16 is not null the block's last
 // gated add writes the bf16 result there instead of updating h.
+// The call's inputs, for its first block: the rows are joined into h in the same pass as the first norm.
+struct FirstRows {
+  const uint16_t* x;
+  const uint16_t* txt;
+};
+
 // Items whose bit is set in skip_items get zero gates, so the block leaves their residual unchanged.
 int run_block(const Ctx& c, const moss_block_weights* w, const float* rope, float* h, uint16_t* out16,
-              unsigned skip_items) {
+              unsigned skip_items, const FirstRows* first) {
   const moss_dims* d = c.d;
   const int B = d->batch, T = d->n_txt + d->n_img, D = d->d_model, F = d->mlp_inner, H = d->n_heads;
   const int R = B * T;
@@ -194,7 +200,12 @@ int run_block(const Ctx& c, const moss_block_weights* w, const float* rope, floa
     StepTimer t(MOSS_STEP_ADALN, st);
     MOSS_TRY(launch_adaln_gemv(s, w->w_mod, mod, B, D, skip_items, st), "adaln_gemv");
   }
-  {
+  if (first) {
+    StepTimer t(MOSS_STEP_JOIN, st);  // row join + the first norm, one pass
+    MOSS_TRY(launch_join_mod_rmsnorm(first->x, first->txt, c.lens, mod + 0 * D, mod + 1 * D, ms, h, a, B, d->n_txt,
+                                     d->n_img, D, d->eps, st),
+             "join_mod_rmsnorm");
+  } else {
     StepTimer t(MOSS_STEP_NORM1, st);
     MOSS_TRY(launch_mod_rmsnorm(h, mod + 0 * D, mod + 1 * D, ms, a, B, T, D, d->eps, st), "mod_rmsnorm");
   }
@@ -284,10 +295,6 @@ int forward(const moss_dims* d, int n_blocks, const uint16_t* x, const uint16_t*
   if (rc != MOSS_OK) return rc;
   c.st = st;
   float* h = reinterpret_cast<float*>(c.ws + c.L.h);
-  {
-    StepTimer t(MOSS_STEP_JOIN, st);
-    MOSS_TRY(launch_join_rows(x, txt, c.lens, h, d->batch, d->n_txt, d->n_img, d->d_model, st), "join_rows");
-  }
   MOSS_TRY(launch_silu_cond(cond, reinterpret_cast<float*>(c.ws + c.L.s_cond), d->batch, d->d_model, st),
            "silu_cond");
   for (int i = 0; i < n_blocks; ++i) {
@@ -295,7 +302,8 @@ int forward(const moss_dims* d, int n_blocks, const uint16_t* x, const uint16_t*
     if (skip)
       for (int b = 0; b < d->batch; ++b)
         if (skip[(size_t)i * d->batch + b]) mask |= 1u << b;
-    rc = run_block(c, &blocks[i], rope, h, i + 1 == n_blocks ? out : nullptr, mask);
+    const FirstRows rows{x, txt};
+    rc = run_block(c, &blocks[i], rope, h, i + 1 == n_blocks ? out : nullptr, mask, i == 0 ? &rows : nullptr);
     if (rc != MOSS_OK) return rc;
   }
   return MOSS_OK;

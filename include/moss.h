@@ -266,7 +266,9 @@ int moss_k_gated_add(int32_t batch, int32_t rows, int32_t d_model, float* h, con
  * moss_stack_forward, in order).  The gated adds and the SiLU gate run in the
  * epilogues of the out, down and up projections: MOSS_STEP_OUT, _UP and _DOWN
  * time the fused launches, and MOSS_STEP_GATE1, _SILU and _GATE2 record
- * nothing. */
+ * nothing.  The row join runs in one pass with the first block's first norm:
+ * MOSS_STEP_JOIN times that pass, and MOSS_STEP_NORM1 the first norms of the
+ * later blocks of a stack. */
 #define MOSS_STEP_JOIN 0
 #define MOSS_STEP_ADALN 1
 #define MOSS_STEP_NORM1 2
