@@ -189,6 +189,35 @@ def normal_f32(seed: int, key: tuple, shape: tuple, std: float) -> np.ndarray:
     return v.reshape(shape)
 
 
+LATENT_DIM = 128   # values per latent row
+ENC_DIM = 4096     # prompt encoder hidden size
+END_NAMES = ("w_t1", "w_t2", "w_txt", "w_in", "w_fmod", "w_final")
+
+
+def make_ends_weights(geom: Geometry, seed: int = 0, enc_dim: int = ENC_DIM, std: float = WEIGHT_STD) -> dict:
+    """The denoiser's end weights as bf16 bits, row-major [out, in]: the timestep
+    MLP w_t1 [D, 256] and w_t2 [D, D], the prompt projection w_txt [D, enc_dim],
+    the latent projection w_in [D, 128], the final modulation w_fmod [2D, D] and
+    the final projection w_final [128, D]; stream group 1000."""
+    d = geom.d_model
+    shapes = {"w_t1": (d, 256), "w_t2": (d, d), "w_txt": (d, enc_dim), "w_in": (d, LATENT_DIM),
+              "w_fmod": (2 * d, d), "w_final": (LATENT_DIM, d)}
+    return {name: normal_bf16(seed, (1000, j), shapes[name], std) for j, name in enumerate(END_NAMES)}
+
+
+def make_denoiser_inputs(geom: Geometry, seed: int = 0, enc_dim: int = ENC_DIM) -> dict:
+    """latent [B, n_img, 128] and prompt rows enc [B, n_txt, enc_dim] (bf16 bits,
+    N(0, 1); pad rows zero), txt_len [B], timesteps t [B] float32 in [0, 1000)."""
+    b = geom.batch
+    latent = normal_bf16(seed, (2000, 0), (b, geom.n_img, LATENT_DIM), ACT_STD)
+    enc = normal_bf16(seed, (2000, 1), (b, geom.n_txt, enc_dim), ACT_STD)
+    lens = np.asarray(geom.lengths(), dtype=np.int32)
+    for i, n in enumerate(lens):
+        enc[i, n:, :] = 0
+    t = np.array([1000.0 * ((0.37 * seed + 0.13 + 0.29 * i) % 1.0) for i in range(b)], dtype=np.float32)
+    return {"latent": latent, "enc": enc, "txt_len": lens, "t": t}
+
+
 def make_tensor(seed: int, tag: int, shape: tuple, std: float = 1.0) -> np.ndarray:
     """An extra test tensor (bf16 bits) on activation stream ``(0, 3 + tag)``."""
     return normal_bf16(seed, (0, 3 + tag), shape, std)

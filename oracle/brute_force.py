@@ -128,3 +128,34 @@ def block_rows(h0, n_valid_txt: int, n_txt: int, cond_b, w, ang, eps: float, hd:
     z = [[_silu(ur[c]) * ur[f + c] for c in range(f)] for ur in u]
     y = _matvec_rows(z, w["w_down"])
     return [[hv + g * yv for hv, g, yv in zip(hr, gate2, yr)] for hr, yr in zip(h1, y)]
+
+
+def denoiser(latent, enc, txt_len, t, ends, blocks, ang, eps: float):
+    """The whole denoiser forward for nested-list inputs, loop by loop.
+
+    latent [B][n_img][128], enc [B][n_txt][E], t [B]; ends holds nested lists
+    w_t1 [D][256], w_t2 [D][D], w_txt [D][E], w_in [D][128], w_fmod [2D][D],
+    w_final [128][D]; blocks is a list of block weight dicts as for ``block``.
+    Returns the velocity [B][n_img][128].  Same readings as oracle.denoiser;
+    the frequencies come from math.pow and each feature is built one at a time."""
+    out = []
+    for b in range(len(latent)):
+        feats = []
+        for i in range(256):
+            w_i = math.pow(10000.0, -(i % 128) / 128.0)
+            feats.append(math.cos(t[b] * w_i) if i < 128 else math.sin(t[b] * w_i))
+        hid = [_silu(v) for v in _matvec_rows([feats], ends["w_t1"])[0]]
+        cond = _matvec_rows([hid], ends["w_t2"])[0]
+        txt_rows = _matvec_rows(enc[b], ends["w_txt"])
+        x_rows = _matvec_rows(latent[b], ends["w_in"])
+        n_txt = len(txt_rows)
+        rows = [list(r) if i < txt_len[b] else [0.0] * len(r) for i, r in enumerate(txt_rows)] + x_rows
+        for w in blocks:
+            rows = block_rows(rows, txt_len[b], n_txt, cond, w, ang, eps, len(w["q_gain"]))
+        d = len(cond)
+        s = [_silu(v) for v in cond]
+        mod = _matvec_rows([s], ends["w_fmod"])[0]
+        shift, scale = mod[:d], mod[d:2 * d]
+        normed = [[v * (1.0 + scale[j]) + shift[j] for j, v in enumerate(_rms(r, eps))] for r in rows[n_txt:]]
+        out.append(_matvec_rows(normed, ends["w_final"]))
+    return out

@@ -15,6 +15,7 @@ import numpy as np
 
 from diffusion_transformer_denoiser_amd import synth
 from oracle import brute_force as bf
+from oracle import denoiser as od
 from oracle import dit_block as ob
 from oracle import sampler as osm
 
@@ -418,6 +419,67 @@ def pin_skip_block():
            ob.join_rows(x, txt, txt_len), 0.0)
 
 
+# ----------------------------------------------------------------------------
+# the denoiser's ends (oracle/denoiser.py)
+# ----------------------------------------------------------------------------
+
+
+def _denoiser_case(geom, seed, enc_dim=64, n_blocks=1, std=0.02):
+    inp = synth.make_denoiser_inputs(geom, seed, enc_dim)
+    ends = {k: ob.widen_bf16(v) for k, v in synth.make_ends_weights(geom, seed, enc_dim, std).items()}
+    ws = [ob.weights_f64(synth.make_block_weights(geom, seed, i)) for i in range(n_blocks)]
+    return ob.widen_bf16(inp["latent"]), ob.widen_bf16(inp["enc"]), inp["txt_len"], inp["t"].astype(np.float64), \
+        ends, ws
+
+
+def pin_timestep_features():
+    """t = 0 gives cos 1 and sin 0 everywhere; feature 0 has frequency 1 and
+    feature 127 frequency 10000^(-127/128) (a half period at t = pi / w);
+    the features' dot product depends on t1 - t2 only (cos a cos b + sin a sin b)."""
+    f0 = od.timestep_features([0.0])[0]
+    assert np.array_equal(f0, np.r_[np.ones(128), np.zeros(128)])
+    w127 = 10000.0 ** (-127.0 / 128.0)
+    f = od.timestep_features([math.pi, math.pi / w127])
+    _close([f[0, 0], f[1, 127], f[0, 128]], [-1.0, -1.0, 0.0], 1e-12)
+    a = od.timestep_features([3.0, 250.0, 600.0, 847.0])
+    _close(a[0] @ a[1], a[2] @ a[3], 1e-10)
+
+
+def pin_denoiser_brute_tiny():
+    """The whole forward == the loop-only twin on tiny geometries (one and two blocks)."""
+    for geom, n_blocks in zip(tiny_geoms(), (1, 2)):
+        lat, enc, lens, t, ends, ws = _denoiser_case(geom, 4, n_blocks=n_blocks, std=0.2)
+        cos, sin = ob.rope_tables(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, geom.head_dim)
+        got = od.denoiser_forward(lat, enc, lens, t, ends, ws, cos, sin, geom.eps)
+        ang = bf.angles(bf.positions(geom.n_txt, geom.grid_h, geom.grid_w), geom.theta, geom.head_dim)
+        ref = bf.denoiser(lat.tolist(), enc.tolist(), [int(n) for n in lens], [float(v) for v in t],
+                          {k: v.tolist() for k, v in ends.items()}, [{k: v.tolist() for k, v in w.items()} for w in ws],
+                          ang, geom.eps)
+        _close(got, np.array(ref), 1e-11)
+
+
+def pin_denoiser_identity_stack():
+    """With every gate zero the stack is the identity: the velocity is the final
+    norm of the latent rows alone, whatever the prompt; and the final norm is
+    scale-invariant in its input rows."""
+    geom = tiny_geoms()[1]
+    lat, enc, lens, t, ends, ws = _denoiser_case(geom, 5, std=0.2)
+    d = geom.d_model
+    for w in ws:
+        w["w_mod"] = w["w_mod"].copy()
+        w["w_mod"][2 * d:3 * d] = 0.0
+        w["w_mod"][5 * d:6 * d] = 0.0
+    cos, sin = ob.rope_tables(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, geom.head_dim)
+    v1 = od.denoiser_forward(lat, enc, lens, t, ends, ws, cos, sin, geom.eps)
+    v2 = od.denoiser_forward(lat, -3.0 * enc + 1.0, lens, t, ends, ws, cos, sin, geom.eps)
+    _close(v1, v2, 1e-12)
+    cond = od.timestep_cond(t, ends["w_t1"], ends["w_t2"])
+    x = lat @ ends["w_in"].T
+    _close(od.final_velocity(x, cond, ends["w_fmod"], ends["w_final"], geom.eps), v1, 1e-12)
+    _close(od.final_velocity(7.0 * x, cond, ends["w_fmod"], ends["w_final"], 1e-30),
+           od.final_velocity(x, cond, ends["w_fmod"], ends["w_final"], 1e-30), 1e-12)
+
+
 ALL_PINS = [
     pin_brute_force_tiny,
     pin_brute_force_stack,
@@ -440,6 +502,9 @@ ALL_PINS = [
     pin_guidance_hand_worked,
     pin_guidance_limits,
     pin_skip_block,
+    pin_timestep_features,
+    pin_denoiser_brute_tiny,
+    pin_denoiser_identity_stack,
 ]
 
 

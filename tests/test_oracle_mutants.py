@@ -9,6 +9,7 @@ planted in the oracle, on the CPU; nothing here touches the GPU library.
 import numpy as np
 import pytest
 
+from oracle import denoiser as od
 from oracle import dit_block as ob
 from oracle import sampler as osm
 
@@ -199,4 +200,52 @@ def test_mutant_is_caught(name, monkeypatch):
 def test_sampler_mutant_is_caught(name, monkeypatch):
     attr, fn = SAMPLER_MUTANTS[name]
     monkeypatch.setattr(osm, attr, fn)
+    assert P.failing_pins(), f"planted mistake {name!r} passed every pin"
+
+
+_orig_den = {name: getattr(od, name) for name in ("timestep_features", "timestep_cond", "final_velocity")}
+
+
+def _features_sin_first(t, n=256):
+    f = _orig_den["timestep_features"](t, n)
+    return np.concatenate([f[:, n // 2:], f[:, :n // 2]], axis=1)
+
+
+def _features_base(t, n=256):
+    t = np.asarray(t, dtype=np.float64).reshape(-1, 1)
+    w = 10000.0 ** (-np.arange(n // 2) / n)
+    return np.concatenate([np.cos(t * w), np.sin(t * w)], axis=1)
+
+
+def _cond_no_silu(t, w_t1, w_t2):
+    return (od.timestep_features(t) @ np.asarray(w_t1).T) @ np.asarray(w_t2).T
+
+
+def _final_raw_cond(h_img, cond, w_fmod, w_final, eps, rnd=lambda a: a):
+    d = h_img.shape[-1]
+    mod = np.asarray(cond, dtype=np.float64) @ np.asarray(w_fmod).T
+    a = rnd(ob.modulated_rmsnorm(h_img, mod[:, None, :d], mod[:, None, d:2 * d], eps))
+    return rnd(a @ np.asarray(w_final).T)
+
+
+def _final_shift_scale_swapped(h_img, cond, w_fmod, w_final, eps, rnd=lambda a: a):
+    d = h_img.shape[-1]
+    mod = ob.silu(np.asarray(cond, dtype=np.float64)) @ np.asarray(w_fmod).T
+    a = rnd(ob.modulated_rmsnorm(h_img, mod[:, None, d:2 * d], mod[:, None, :d], eps))
+    return rnd(a @ np.asarray(w_final).T)
+
+
+DENOISER_MUTANTS = {
+    "features_sin_half_first": ("timestep_features", _features_sin_first),
+    "features_frequency_base": ("timestep_features", _features_base),
+    "timestep_mlp_without_silu": ("timestep_cond", _cond_no_silu),
+    "final_modulation_without_silu": ("final_velocity", _final_raw_cond),
+    "final_shift_scale_swapped": ("final_velocity", _final_shift_scale_swapped),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DENOISER_MUTANTS))
+def test_denoiser_mutant_is_caught(name, monkeypatch):
+    attr, fn = DENOISER_MUTANTS[name]
+    monkeypatch.setattr(od, attr, fn)
     assert P.failing_pins(), f"planted mistake {name!r} passed every pin"
