@@ -66,3 +66,8 @@ __device__ __forceinline__ float group_sum(float v) {
 struct ItemLens {
   int32_t len[MOSS_MAX_BATCH];
 };
+
+// Per-item timesteps, passed to a kernel by value.
+struct ItemTimes {
+  float t[MOSS_MAX_BATCH];
+};

@@ -282,6 +282,31 @@ __global__ __launch_bounds__(kThreads) void guidance_euler_kernel(const u32x4* _
   }
 }
 
+// ---- the denoiser's ends ------------------------------------------------------
+// 256 timestep features per item: cos(t w_i) for i < 128, then sin(t w_i),
+// w_i = 10000^(-i/128), with the angle and its cos/sin in fp64, stored fp32.
+__global__ __launch_bounds__(kThreads) void timestep_features_kernel(ItemTimes ts, float* __restrict__ f,
+                                                                     int batch) {
+  const int idx = blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= batch * 256) return;
+  const int b = idx >> 8, i = idx & 255, j = i & 127;
+  const double ang = (double)ts.t[b] * exp(-(double)j / 128.0 * log(10000.0));
+  f[idx] = (float)(i < 128 ? cos(ang) : sin(ang));
+}
+
+// y = SiLU(x) in fp32 (in place allowed).
+__global__ __launch_bounds__(kThreads) void silu_f32_kernel(const float* x, float* y, int n) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) y[i] = silu_f32(x[i]);
+}
+
+// bf16 (round to nearest even) of fp32 values.
+__global__ __launch_bounds__(kThreads) void round_bf16_kernel(const float* __restrict__ x, uint16_t* __restrict__ y,
+                                                              int n) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) y[i] = __builtin_bit_cast(uint16_t, (__bf16)x[i]);
+}
+
 // ---- rotary tables ------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void rope_build_kernel(int n_txt, int grid_w, double theta, float* rope,
                                                               int rows) {
@@ -414,5 +439,37 @@ hipError_t launch_join_mod_rmsnorm(const uint16_t* x, const uint16_t* txt, const
   else
     hipLaunchKernelGGL(join_mod_rmsnorm_kernel<16>, grid, block, 0, st, xv, tv, lens, shift, scale, mod_stride, h,
                        out, n_txt, n_img, d, eps, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv(const float* x, const uint16_t* w, float* y, int batch, int d_in, int n_out, hipStream_t st) {
+  const int cpl = (d_in / 8 + 63) / 64;
+  const dim3 grid((n_out + 3) / 4), block(kThreads);
+  if (cpl <= 2)
+    hipLaunchKernelGGL(adaln_gemv_kernel<2>, grid, block, 0, st, x, w, y, batch, n_out, d_in, 0u);
+  else if (cpl <= 4)
+    hipLaunchKernelGGL(adaln_gemv_kernel<4>, grid, block, 0, st, x, w, y, batch, n_out, d_in, 0u);
+  else if (cpl <= 6)
+    hipLaunchKernelGGL(adaln_gemv_kernel<6>, grid, block, 0, st, x, w, y, batch, n_out, d_in, 0u);
+  else if (cpl <= 8)
+    hipLaunchKernelGGL(adaln_gemv_kernel<8>, grid, block, 0, st, x, w, y, batch, n_out, d_in, 0u);
+  else
+    hipLaunchKernelGGL(adaln_gemv_kernel<16>, grid, block, 0, st, x, w, y, batch, n_out, d_in, 0u);
+  return hipGetLastError();
+}
+
+hipError_t launch_timestep_features(const ItemTimes& ts, float* f, int batch, hipStream_t st) {
+  hipLaunchKernelGGL(timestep_features_kernel, dim3((batch * 256 + kThreads - 1) / kThreads), dim3(kThreads), 0, st,
+                     ts, f, batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_f32(const float* x, float* y, int n, hipStream_t st) {
+  hipLaunchKernelGGL(silu_f32_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, st, x, y, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_round_bf16(const float* x, uint16_t* y, int n, hipStream_t st) {
+  hipLaunchKernelGGL(round_bf16_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, st, x, y, n);
   return hipGetLastError();
 }

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 struct ItemLens;
+struct ItemTimes;
 
 hipError_t launch_join_rows(const uint16_t* x, const uint16_t* txt, const ItemLens& lens, float* out, int batch,
                             int n_txt, int n_img, int d, hipStream_t st);
@@ -50,3 +51,10 @@ hipError_t launch_qk_norm_rope_pack(int batch, int rows, int n_heads, float eps,
                                     uint16_t* q, uint16_t* k, uint16_t* v, hipStream_t st);
 hipError_t launch_attention(int batch, int n_heads, int rows, int n_txt, const ItemLens& lens, const uint16_t* q,
                             const uint16_t* k, const uint16_t* v, uint16_t* o, hipStream_t st);
+
+// The denoiser's ends: y[b, :n_out] = W x[b] (W [n_out, d_in] bf16, x fp32, d_in % 8 == 0);
+// 256 sinusoidal timestep features per item; SiLU in fp32 (in place allowed); fp32 -> bf16.
+hipError_t launch_gemv(const float* x, const uint16_t* w, float* y, int batch, int d_in, int n_out, hipStream_t st);
+hipError_t launch_timestep_features(const ItemTimes& ts, float* f, int batch, hipStream_t st);
+hipError_t launch_silu_f32(const float* x, float* y, int n, hipStream_t st);
+hipError_t launch_round_bf16(const float* x, uint16_t* y, int n, hipStream_t st);

@@ -284,7 +284,28 @@ int validate_forward(const moss_dims* d, int n_blocks, const uint16_t* x, const 
   return MOSS_OK;
 }
 
-// skip: null, or host [n_blocks][batch], nonzero where block i is not applied to item b.
+// The stack on validated arguments: cond's SiLU, then the blocks; the first
+// block joins x and txt into h, the last writes bf16 `out` (or, with out
+// null, leaves its result in the fp32 residual h).  skip: null, or host
+// [n_blocks][batch], nonzero where block i is not applied to item b.
+int run_stack(const Ctx& c, int n_blocks, const uint16_t* x, const uint16_t* txt, const uint16_t* cond,
+              const moss_block_weights* blocks, const float* rope, uint16_t* out, const uint8_t* skip) {
+  const moss_dims* d = c.d;
+  float* h = reinterpret_cast<float*>(c.ws + c.L.h);
+  MOSS_TRY(launch_silu_cond(cond, reinterpret_cast<float*>(c.ws + c.L.s_cond), d->batch, d->d_model, c.st),
+           "silu_cond");
+  for (int i = 0; i < n_blocks; ++i) {
+    unsigned mask = 0;
+    if (skip)
+      for (int b = 0; b < d->batch; ++b)
+        if (skip[(size_t)i * d->batch + b]) mask |= 1u << b;
+    const FirstRows rows{x, txt};
+    const int rc = run_block(c, &blocks[i], rope, h, i + 1 == n_blocks ? out : nullptr, mask, i == 0 ? &rows : nullptr);
+    if (rc != MOSS_OK) return rc;
+  }
+  return MOSS_OK;
+}
+
 int forward(const moss_dims* d, int n_blocks, const uint16_t* x, const uint16_t* txt, const int32_t* txt_len,
             const uint16_t* cond, const moss_block_weights* blocks, const float* rope, uint16_t* out,
             void* workspace, size_t ws_bytes, hipStream_t st, const uint8_t* skip = nullptr) {
@@ -294,18 +315,119 @@ int forward(const moss_dims* d, int n_blocks, const uint16_t* x, const uint16_t*
   rc = check_current_device();
   if (rc != MOSS_OK) return rc;
   c.st = st;
-  float* h = reinterpret_cast<float*>(c.ws + c.L.h);
-  MOSS_TRY(launch_silu_cond(cond, reinterpret_cast<float*>(c.ws + c.L.s_cond), d->batch, d->d_model, st),
-           "silu_cond");
-  for (int i = 0; i < n_blocks; ++i) {
-    unsigned mask = 0;
-    if (skip)
-      for (int b = 0; b < d->batch; ++b)
-        if (skip[(size_t)i * d->batch + b]) mask |= 1u << b;
-    const FirstRows rows{x, txt};
-    rc = run_block(c, &blocks[i], rope, h, i + 1 == n_blocks ? out : nullptr, mask, i == 0 ? &rows : nullptr);
-    if (rc != MOSS_OK) return rc;
+  return run_stack(c, n_blocks, x, txt, cond, blocks, rope, out, skip);
+}
+
+// ---- the whole denoiser forward ---------------------------------------------------
+constexpr int kLatent = 128;  // values per latent row
+constexpr int kFreq = 256;    // timestep features
+
+// The ends' scratch, after the stack's plan: the projected rows the stack
+// joins (bf16), cond (fp32 and bf16), the timestep MLP's hidden values and the
+// final modulation (fp32).
+struct EndsLayout {
+  size_t xrows, trows, cond32, cond16, feat, hid, modf, total;
+};
+EndsLayout plan_ends(const moss_dims* d, size_t start) {
+  EndsLayout E;
+  const size_t B = d->batch, D = d->d_model;
+  size_t off = start;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += round256(bytes);
+    return o;
+  };
+  E.xrows = take(2 * B * d->n_img * D);
+  E.trows = take(2 * B * (size_t)d->n_txt * D);
+  E.cond32 = take(4 * B * D);
+  E.cond16 = take(2 * B * D);
+  E.feat = take(4 * B * kFreq);
+  E.hid = take(4 * B * D);
+  E.modf = take(4 * B * 2 * D);
+  E.total = off;
+  return E;
+}
+
+bool ends_ok(const moss_denoiser_weights* e) {
+  if (!e || e->enc_dim < 64 || e->enc_dim % 64 || e->enc_dim > 16384) return false;
+  const void* p[] = {e->w_t1, e->w_t2, e->w_txt, e->w_in, e->w_fmod, e->w_final};
+  for (const void* q : p)
+    if (!q || !aligned16(q)) return false;
+  return true;
+}
+
+int denoiser(const moss_dims* d, int n_blocks, const uint16_t* latent, const uint16_t* enc, const int32_t* txt_len,
+             const float* t, const moss_denoiser_weights* e, const moss_block_weights* blocks, const uint8_t* skip,
+             const float* rope, uint16_t* velocity, void* workspace, size_t ws_bytes, hipStream_t st) {
+  if (!dims_ok(d) || d->n_img < 1 || n_blocks < 1 || !blocks || !ends_ok(e) || !t) return MOSS_EINVAL;
+  if (!latent || !aligned16(latent) || !rope || !aligned16(rope) || !velocity || !aligned16(velocity))
+    return MOSS_EINVAL;
+  if (d->n_txt > 0 && (!enc || !aligned16(enc))) return MOSS_EINVAL;
+  ItemTimes ts{};
+  for (int b = 0; b < d->batch; ++b) {
+    if (!isfinite(t[b])) return MOSS_EINVAL;
+    ts.t[b] = t[b];
   }
+  Ctx c;
+  if (!lens_ok(d, txt_len, &c.lens)) return MOSS_EINVAL;
+  for (int i = 0; i < n_blocks; ++i)
+    if (!weights_ok(&blocks[i])) return MOSS_EINVAL;
+  if (!workspace || !aligned16(workspace)) return MOSS_EWORKSPACE;
+  c.L = plan(d);
+  const EndsLayout E = plan_ends(d, c.L.total);
+  if (ws_bytes < E.total) return MOSS_EWORKSPACE;
+  const size_t B = d->batch, T = (size_t)d->n_txt + d->n_img, D = d->d_model, F = d->mlp_inner;
+  const size_t vb = 2 * B * d->n_img * kLatent, ed = e->enc_dim;
+  const void* in[] = {latent, enc, rope, workspace, e->w_t1, e->w_t2, e->w_txt, e->w_in, e->w_fmod, e->w_final};
+  const size_t len[] = {2 * B * d->n_img * kLatent, 2 * B * d->n_txt * ed, 4 * 2 * T * 64, E.total, 2 * D * kFreq,
+                        2 * D * D, 2 * D * ed, 2 * D * kLatent, 2 * 2 * D * D, 2 * kLatent * D};
+  for (int i = 0; i < 10; ++i)
+    if (overlaps(velocity, vb, in[i], len[i])) return MOSS_EALIAS;
+  for (int i = 0; i < n_blocks; ++i) {
+    const moss_block_weights& w = blocks[i];
+    if (overlaps(velocity, vb, w.w_mod, 2 * 6 * D * D) || overlaps(velocity, vb, w.w_qkv, 2 * 3 * D * D) ||
+        overlaps(velocity, vb, w.q_gain, 256) || overlaps(velocity, vb, w.k_gain, 256) ||
+        overlaps(velocity, vb, w.w_out, 2 * D * D) || overlaps(velocity, vb, w.w_up, 2 * 2 * F * D) ||
+        overlaps(velocity, vb, w.w_down, 2 * D * F))
+      return MOSS_EALIAS;
+  }
+  int rc = check_current_device();
+  if (rc != MOSS_OK) return rc;
+  c.d = d;
+  c.ws = static_cast<char*>(workspace);
+  c.st = st;
+  const int Bi = d->batch, Di = d->d_model;
+  float* feat = reinterpret_cast<float*>(c.ws + E.feat);
+  float* hid = reinterpret_cast<float*>(c.ws + E.hid);
+  float* cond32 = reinterpret_cast<float*>(c.ws + E.cond32);
+  uint16_t* cond16 = reinterpret_cast<uint16_t*>(c.ws + E.cond16);
+  uint16_t* xrows = reinterpret_cast<uint16_t*>(c.ws + E.xrows);
+  uint16_t* trows = reinterpret_cast<uint16_t*>(c.ws + E.trows);
+  // cond = bf16(W_t2 SiLU(W_t1 features(t)))
+  MOSS_TRY(launch_timestep_features(ts, feat, Bi, st), "timestep_features");
+  MOSS_TRY(launch_gemv(feat, e->w_t1, hid, Bi, kFreq, Di, st), "gemv t1");
+  MOSS_TRY(launch_silu_f32(hid, hid, Bi * Di, st), "silu");
+  MOSS_TRY(launch_gemv(hid, e->w_t2, cond32, Bi, Di, Di, st), "gemv t2");
+  MOSS_TRY(launch_round_bf16(cond32, cond16, Bi * Di, st), "round cond");
+  // the rows the stack joins
+  MOSS_TRY(launch_gemm_nt(Bi * d->n_img, Di, kLatent, latent, kLatent, e->w_in, kLatent, xrows, Di, st),
+           "gemm latent rows");
+  if (d->n_txt > 0)
+    MOSS_TRY(launch_gemm_nt(Bi * d->n_txt, Di, (int)ed, enc, (int)ed, e->w_txt, (int)ed, trows, Di, st),
+             "gemm prompt rows");
+  rc = run_stack(c, n_blocks, xrows, trows, cond16, blocks, rope, nullptr, skip);
+  if (rc != MOSS_OK) return rc;
+  // velocity = W_final modnorm(h_img; W_fmod SiLU(cond)); the stack left SiLU(cond) in s_cond
+  float* modf = reinterpret_cast<float*>(c.ws + E.modf);
+  float* h = reinterpret_cast<float*>(c.ws + c.L.h);
+  uint16_t* a = reinterpret_cast<uint16_t*>(c.ws + c.L.a);
+  MOSS_TRY(launch_gemv(reinterpret_cast<float*>(c.ws + c.L.s_cond), e->w_fmod, modf, Bi, Di, 2 * Di, st),
+           "gemv final modulation");
+  MOSS_TRY(launch_mod_rmsnorm(h, modf, modf + Di, 2 * Di, a, Bi, (int)T, Di, d->eps, st), "final norm");
+  for (int b = 0; b < Bi; ++b)
+    MOSS_TRY(launch_gemm_nt(d->n_img, kLatent, Di, a + ((size_t)b * T + d->n_txt) * D, Di, e->w_final, Di,
+                            velocity + (size_t)b * d->n_img * kLatent, kLatent, st),
+             "gemm velocity");
   return MOSS_OK;
 }
 
@@ -366,6 +488,19 @@ int moss_stack_forward_skip(const moss_dims* dims, int32_t n_blocks, const uint1
                             const uint8_t* skip, const float* rope, uint16_t* out, void* workspace,
                             size_t ws_bytes, hipStream_t stream) {
   return forward(dims, n_blocks, x, txt, txt_len, cond, blocks, rope, out, workspace, ws_bytes, stream, skip);
+}
+
+size_t moss_denoiser_workspace_bytes(const moss_dims* dims, int32_t n_blocks) {
+  if (!dims_ok(dims) || n_blocks < 1 || dims->n_img < 1) return 0;
+  return plan_ends(dims, plan(dims).total).total;
+}
+
+int moss_denoiser_forward(const moss_dims* dims, int32_t n_blocks, const uint16_t* latent, const uint16_t* enc,
+                          const int32_t* txt_len, const float* t, const moss_denoiser_weights* ends,
+                          const moss_block_weights* blocks, const uint8_t* skip, const float* rope,
+                          uint16_t* velocity, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return denoiser(dims, n_blocks, latent, enc, txt_len, t, ends, blocks, skip, rope, velocity, workspace, ws_bytes,
+                  stream);
 }
 
 int moss_guidance_euler(int32_t rows, int32_t width, const uint16_t* v_pos, const uint16_t* v_neg, float guidance,

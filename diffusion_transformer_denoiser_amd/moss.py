@@ -36,6 +36,13 @@ class moss_block_weights(ctypes.Structure):
     _fields_ = [(n, c_vp) for n in WEIGHT_FIELDS]
 
 
+END_FIELDS = ("w_t1", "w_t2", "w_txt", "w_in", "w_fmod", "w_final")
+
+
+class moss_denoiser_weights(ctypes.Structure):
+    _fields_ = [(n, c_vp) for n in END_FIELDS] + [("enc_dim", ctypes.c_int32)]
+
+
 class MossError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -55,6 +62,10 @@ _SIGS = {
     "moss_stack_forward_skip": (ctypes.c_int, [ctypes.POINTER(moss_dims), c_i32, c_vp, c_vp, c_vp, c_vp,
                                                ctypes.POINTER(moss_block_weights), c_vp, c_vp, c_vp, c_vp, c_size,
                                                c_vp]),
+    "moss_denoiser_workspace_bytes": (c_size, [ctypes.POINTER(moss_dims), c_i32]),
+    "moss_denoiser_forward": (ctypes.c_int, [ctypes.POINTER(moss_dims), c_i32, c_vp, c_vp, c_vp, c_vp,
+                                             ctypes.POINTER(moss_denoiser_weights), ctypes.POINTER(moss_block_weights),
+                                             c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "moss_guidance_euler": (ctypes.c_int, [c_i32, c_i32, c_vp, c_vp, c_f32, c_f32, c_vp, c_vp, c_vp]),
     "moss_k_join_rows": (ctypes.c_int, [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moss_k_adaln_gemv": (ctypes.c_int, [c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
@@ -203,6 +214,37 @@ def moss_stack_forward_skip(dims, blocks, skip, x, txt, txt_len, cond, rope, out
                                        workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                        _s(stream))
     _check(rc, "moss_stack_forward_skip")
+
+
+def make_ends(e: dict, enc_dim: int) -> moss_denoiser_weights:
+    """The ends' weight struct; it keeps the tensors alive as long as it lives."""
+    s = moss_denoiser_weights(*[_p(e[n]) for n in END_FIELDS], enc_dim)
+    s._tensors = [e[n] for n in END_FIELDS]
+    return s
+
+
+def moss_denoiser_workspace_bytes(dims, n_blocks) -> int:
+    return lib().moss_denoiser_workspace_bytes(ctypes.byref(dims), n_blocks)
+
+
+def moss_denoiser_forward(dims, blocks, latent, enc, txt_len, t, ends, enc_dim, rope, velocity, workspace,
+                          skip=None, stream=None) -> None:
+    """``ends``: a dict of the six end weights (or a moss_denoiser_weights); ``t``: per-item timesteps."""
+    arr = (moss_block_weights * len(blocks))(
+        *[b if isinstance(b, moss_block_weights) else make_weights(b) for b in blocks])
+    e = ends if isinstance(ends, moss_denoiser_weights) else make_ends(ends, enc_dim)
+    ts = (ctypes.c_float * len(t))(*[float(v) for v in t])
+    sk = None
+    if skip is not None:
+        flat = [1 if f else 0 for row in skip for f in row]
+        flags = (ctypes.c_uint8 * len(flat))(*flat)  # alive until the call returns
+        sk = ctypes.cast(flags, c_vp)
+    rc = lib().moss_denoiser_forward(ctypes.byref(dims), len(blocks), _p(latent), _p(enc),
+                                     ctypes.cast(_lens(txt_len), c_vp), ctypes.cast(ts, c_vp), ctypes.byref(e), arr, sk,
+                                     _p(rope), _p(velocity), _p(workspace),
+                                     workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                     _s(stream))
+    _check(rc, "moss_denoiser_forward")
 
 
 def moss_guidance_euler(rows, width, v_pos, v_neg, guidance, dsigma, x_in, x_out, stream=None) -> None:

@@ -170,6 +170,47 @@ int moss_stack_forward_skip(const moss_dims* dims, int32_t n_blocks, const uint1
 int moss_guidance_euler(int32_t rows, int32_t width, const uint16_t* v_pos, const uint16_t* v_neg, float guidance,
                         float dsigma, const float* x_in, float* x_out, hipStream_t stream);
 
+/* ---- the whole denoiser forward (the ends around the stack) ------------- */
+
+/* Weights of the denoiser's ends, bf16 bits, row-major [out, in] (device;
+ * caller-owned).  The pages name these parts and sizes, not their formulas
+ * (the MOSS-Image transformer page, TensorFold PR #1528, "What it adds": the
+ * timestep's modulation; the encoder page, PR #1512: hidden size 4096; the
+ * CUDA port page, PR #2281: latents of 128 values per row); each takes the
+ * standard DiT form without biases. */
+typedef struct {
+  const uint16_t* w_t1;    /* [D, 256]: timestep features -> hidden */
+  const uint16_t* w_t2;    /* [D, D]: SiLU(hidden) -> cond */
+  const uint16_t* w_txt;   /* [D, enc_dim]: prompt rows -> model width */
+  const uint16_t* w_in;    /* [D, 128]: latent rows -> model width */
+  const uint16_t* w_fmod;  /* [2D, D]: SiLU(cond) -> final (shift, scale) */
+  const uint16_t* w_final; /* [128, D]: normed image rows -> velocity */
+  int32_t enc_dim;         /* prompt row width (4096 for the released encoder); % 64 == 0, <= 16384 */
+} moss_denoiser_weights;
+
+/* Workspace bytes for moss_denoiser_forward with these dims (the stack's plan
+ * plus the ends' scratch); 0 when the dims are invalid or n_img < 1. */
+size_t moss_denoiser_workspace_bytes(const moss_dims* dims, int32_t n_blocks);
+
+/* One denoiser forward: velocity = f(latent, prompt rows, t).
+ *   features = cos(t w_i), i < 128, then sin(t w_i), w_i = 10000^(-i/128);
+ *   cond = bf16(W_t2 SiLU(W_t1 features));
+ *   txt = bf16(enc W_txt^T), x = bf16(latent W_in^T);
+ *   h = the block stack on (x, txt, cond), kept in fp32 (skip as in
+ *       moss_stack_forward_skip, may be NULL);
+ *   velocity = bf16(bf16(modRMSNorm(h_image_rows; shift, scale)) W_final^T),
+ *       (shift, scale) = W_fmod SiLU(cond).
+ * latent [B, n_img, 128] bf16, enc [B, n_txt, enc_dim] bf16 (rows at or past
+ * txt_len[b] are never read; NULL when n_txt == 0), t host [B] (finite; the
+ * pipeline's timestep scale, e.g. 1000 sigma), velocity [B, n_img, 128] bf16,
+ * all device pointers 16-byte aligned.  rope, txt_len, blocks and the error
+ * codes as moss_stack_forward; velocity must not overlap any input, weight
+ * or the workspace (MOSS_EALIAS); n_img >= 1. */
+int moss_denoiser_forward(const moss_dims* dims, int32_t n_blocks, const uint16_t* latent, const uint16_t* enc,
+                          const int32_t* txt_len, const float* t, const moss_denoiser_weights* ends,
+                          const moss_block_weights* blocks, const uint8_t* skip, const float* rope,
+                          uint16_t* velocity, void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* ---- single-step entry points (same conventions; used by the tests) ----- */
 
 /* Packed attention layouts written by moss_k_qk_norm_rope_pack and read by

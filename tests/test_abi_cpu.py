@@ -217,3 +217,49 @@ def test_stack_skip_validates():
                                        ctypes.cast(flags, ctypes.c_void_p), fake(4), fake(5), fake(6),
                                        moss.moss_workspace_bytes(d, 1), None)
         assert rc == moss.MOSS_EDEVICE
+
+
+def _ends(enc_dim=4096, base_slot=30):
+    return moss.moss_denoiser_weights(*[fake(base_slot + i) for i in range(6)], enc_dim)
+
+
+def denoiser(dims, n_blocks=1, ends=None, latent=None, enc=None, t=(500.0,), vel=None, ws=None, ws_bytes=None,
+             lens=None):
+    L = moss.lib()
+    if ws_bytes is None:
+        ws_bytes = moss.moss_denoiser_workspace_bytes(dims, n_blocks)
+    ts = (ctypes.c_float * len(t))(*t)
+    blocks = (moss.moss_block_weights * n_blocks)(*[weights() for _ in range(n_blocks)])
+    ln = None if lens is None else ctypes.cast((ctypes.c_int32 * len(lens))(*lens), ctypes.c_void_p)
+    return L.moss_denoiser_forward(ctypes.byref(dims), n_blocks, fake(1) if latent is None else latent,
+                                   fake(2) if enc is None else enc, ln, ctypes.cast(ts, ctypes.c_void_p),
+                                   ctypes.byref(ends or _ends()), blocks, None, fake(4), fake(5) if vel is None else vel,
+                                   fake(6) if ws is None else ws, ws_bytes, None)
+
+
+def test_denoiser_workspace_bytes():
+    d = c2_dims()
+    assert moss.moss_denoiser_workspace_bytes(d, 1) > moss.moss_workspace_bytes(d, 1)
+    assert moss.moss_denoiser_workspace_bytes(c2_dims(n_img=0, n_txt=8), 1) == 0
+    assert moss.moss_denoiser_workspace_bytes(d, 0) == 0
+
+
+def test_denoiser_validates():
+    d = c2_dims()
+    assert denoiser(d, ends=_ends(enc_dim=100)) == moss.MOSS_EINVAL
+    assert denoiser(d, ends=_ends(enc_dim=0)) == moss.MOSS_EINVAL
+    assert denoiser(d, t=(float("nan"),)) == moss.MOSS_EINVAL
+    assert denoiser(d, latent=0) == moss.MOSS_EINVAL
+    assert denoiser(d, latent=fake(1, 8)) == moss.MOSS_EINVAL
+    assert denoiser(d, n_blocks=0) == moss.MOSS_EINVAL
+    assert denoiser(c2_dims(n_img=0, n_txt=8), lens=[8]) == moss.MOSS_EINVAL
+    e = _ends()
+    e.w_final = None
+    assert denoiser(d, ends=e) == moss.MOSS_EINVAL
+    need = moss.moss_denoiser_workspace_bytes(d, 1)
+    assert denoiser(d, ws_bytes=need - 1) == moss.MOSS_EWORKSPACE
+    assert denoiser(d, vel=fake(6, 4096)) == moss.MOSS_EALIAS  # velocity inside the workspace
+    assert denoiser(d, vel=fake(1, 256)) == moss.MOSS_EALIAS  # velocity over the latent
+    assert denoiser(d, vel=fake(35, 0)) == moss.MOSS_EALIAS  # velocity over w_final
+    if moss.moss_device_check(0) != moss.MOSS_OK:
+        assert denoiser(d) == moss.MOSS_EDEVICE
