@@ -3,10 +3,12 @@
 // adds" and "Shared code": the head-128 instance of the full vision attention,
 // softmax in fp32).
 //
-// gfx950 design.  A workgroup owns 128 queries of one (item, head); each of
-// its four wavefronts owns 32 queries and keeps them in registers as MFMA
-// operands for the whole key loop.  Two workgroups share a CU (2 wavefronts
-// per SIMD), so one wavefront's softmax overlaps the other's MFMAs.
+// gfx950 design.  A workgroup owns 256 queries of one (item, head); each of
+// its eight wavefronts owns 32 queries and keeps them in registers as MFMA
+// operands for the whole key loop.  One workgroup fills a CU (2 wavefronts
+// per SIMD), so one wavefront's softmax overlaps the other's MFMAs, and each
+// K/V tile is loaded into LDS once for 256 queries (a 128-query workgroup,
+// two per CU, loaded every tile twice per CU and ran 1% slower overall).
 //
 //  * Keys advance 64 at a time through two LDS stages (K rows, and V
 //    transposed as the q/k kernel packs it), each filled straight from
@@ -48,9 +50,14 @@ namespace {
 #define MOSS_ATTN_SCHED 4
 #endif
 
-constexpr int BQ = 128;  // queries per workgroup
+#ifndef MOSS_ATTN_WAVES
+#define MOSS_ATTN_WAVES 8
+#endif
+constexpr int NWV = MOSS_ATTN_WAVES;  // wavefronts per workgroup, 32 queries each
+constexpr int BQ = 32 * NWV;         // queries per workgroup
+constexpr int LPW = 16 / NWV;        // 1 KiB direct loads per wavefront per K (and per V) tile
 constexpr int BKV = 64;  // keys per tile
-constexpr int kThreads = 256;
+constexpr int kThreads = 64 * NWV;
 constexpr int kStage = 32768;  // K tile (16 KiB) then V^T tile (16 KiB)
 constexpr float kLazy = 8.0f;  // log2-unit growth of a row max that forces a rescale
 
@@ -63,7 +70,7 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const uint16_t* __restrict__ qp,
+__global__ __launch_bounds__(kThreads, 8 / NWV) void attn_fwd_kernel(const uint16_t* __restrict__ qp,
                                                                const uint16_t* __restrict__ kp,
                                                                const uint16_t* __restrict__ vp,
                                                                uint16_t* __restrict__ o, int rows, int rows_pad,
@@ -83,17 +90,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const uint16_t* _
   const int qrow = qt * BQ + wave * 32 + l32;
   bf16x8 qf[8];
   {
-    const u32x4* src = reinterpret_cast<const u32x4*>(qb + (size_t)qrow * 128);
+    // a workgroup may extend past the packed rows when BQ > 128: those lanes re-read the last packed
+    // row and store nothing
+    const u32x4* src = reinterpret_cast<const u32x4*>(qb + (size_t)min(qrow, rows_pad - 1) * 128);
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = __builtin_bit_cast(bf16x8, src[2 * s + hh]);
   }
 
   // direct-to-LDS load sources: instruction i of this wavefront fills 1 KiB block (wave + 4i)
   // of the K tile (4 key rows of 256 B) and of the V^T tile (8 dim rows of 128 B)
-  int koff[4], voff[4];
+  int koff[LPW], voff[LPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int blk = wave + 4 * i;
+  for (int i = 0; i < LPW; ++i) {
+    const int blk = wave + NWV * i;
     const int key = blk * 4 + (lane >> 4);
     koff[i] = key * 128 + (((lane & 15) ^ (key & 15)) * 8);
     const int dim = blk * 8 + (lane >> 3);
@@ -104,11 +113,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const uint16_t* _
     const uint16_t* ks = kb + (size_t)kt * BKV * 128;
     const uint16_t* vs = vb + (size_t)kt * BKV * 128;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_global_load_lds((const void*)(ks + koff[i]), (MOSS_LDS void*)(base + 1024 * (wave + 4 * i)),
+    for (int i = 0; i < LPW; ++i) {
+      __builtin_amdgcn_global_load_lds((const void*)(ks + koff[i]), (MOSS_LDS void*)(base + 1024 * (wave + NWV * i)),
                                        16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(vs + voff[i]),
-                                       (MOSS_LDS void*)(base + 16384 + 1024 * (wave + 4 * i)), 16, 0, 0);
+                                       (MOSS_LDS void*)(base + 16384 + 1024 * (wave + NWV * i)), 16, 0, 0);
     }
   };
   // this lane's fragment offsets within a stage
@@ -266,7 +275,7 @@ hipError_t launch_attention(int batch, int n_heads, int rows, int n_txt, const I
                             const uint16_t* k, const uint16_t* v, uint16_t* o, hipStream_t st) {
   const int rp = packed_rows(rows);
   const float scale_log2 = (float)(1.4426950408889634 / sqrt(128.0));
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(rp / BQ, n_heads, batch), dim3(kThreads), 0, st, q, k, v, o, rows, rp,
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3((rp + BQ - 1) / BQ, n_heads, batch), dim3(kThreads), 0, st, q, k, v, o, rows, rp,
                      n_heads, n_txt, lens, scale_log2);
   return hipGetLastError();
 }
