@@ -64,6 +64,8 @@ def parse():
                    help="skip the per-step, repeat-hash and 24-block stack measurements after the main timing")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one plain 256 MiB device copy before the warm-up (for counter runs)")
+    p.add_argument("--oracle-sweep", action="store_true",
+                   help="time the float64 oracle on the c0-c3 blocks and two c4 blocks (CPU only), then exit")
     p.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="write the HBM traffic summary from two rocprofv3 --pmc CSV runs, then exit")
     return p.parse_args()
@@ -218,7 +220,8 @@ def step_work(geom):
     m, d, f = geom.batch * geom.rows, geom.d_model, geom.mlp_inner
     t = geom.rows
     return {
-        "JOIN": (0.0, (2 * m * d + 4 * m * d) / 1e6),
+        # the row join runs in one pass with the first block's first norm: x/txt in, h (fp32) and a (bf16) out
+        "JOIN": (0.0, (2 * m * d + 4 * m * d + 2 * m * d) / 1e6),
         "ADALN": (2 * geom.batch * 6 * d * d / 1e9, 2 * 6 * d * d / 1e6),
         "NORM1": (0.0, (4 * m * d + 2 * m * d) / 1e6),
         "QKV": (2 * m * 3 * d * d / 1e9, None),
@@ -245,7 +248,10 @@ def per_step(torch, moss, step, geom, reps=5, cold=False):
             step()
         torch.cuda.synchronize()
         ms = moss.moss_probe_collect(reps)
-        us = 1000.0 * float(np.mean(ms)) if ms else float("nan")
+        if not ms:  # a step with no launch of its own in a single block (the first norm runs with the join)
+            res[name.lower()] = None
+            continue
+        us = 1000.0 * float(np.mean(ms))
         gflop, mb = work[name]
         entry = {"us": round(us, 2)}
         if gflop:
@@ -338,6 +344,41 @@ def stack_timing(torch, moss, geom, seed, reps=3):
                                      "(128-wide) projections, final norm and velocity projection"}
 
 
+def oracle_sweep():
+    """Time the float64 oracle on one block at each workload (c0-c3) and on two blocks of the
+    24-block guidance pair (c4; the 24-block time is 12x that), on this host's cores."""
+    import platform
+    from diffusion_transformer_denoiser_amd import synth
+    from oracle import dit_block as ob
+    threads = len(os.sched_getaffinity(0))
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    rows = []
+    for name, n_blocks in (("c0", 1), ("c1", 1), ("c2", 1), ("c3", 1), ("c4", 2)):
+        geom = synth.CONFIGS[name]
+        acts = synth.make_activations(geom, 0)
+        ws = [ob.weights_f64(synth.make_block_weights(geom, 0, i)) for i in range(n_blocks)]
+        cos, sin = ob.rope_tables(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, geom.head_dim)
+        x, txt, cond = ob.widen_bf16(acts["x"]), ob.widen_bf16(acts["txt"]), ob.widen_bf16(acts["cond"])
+        t0 = time.perf_counter()
+        ob.stack_forward(x, txt, acts["txt_len"], cond, ws, cos, sin, geom.eps)
+        dt = time.perf_counter() - t0
+        per_block = dt / n_blocks
+        rows.append((name, geom.batch, geom.rows, n_blocks, dt, per_block, geom.block_flops() / per_block / 1e9))
+        print(f"oracle {name}: {n_blocks} block(s) in {dt:.2f} s", file=sys.stderr, flush=True)
+    print(f"float64 oracle on {threads} threads of {cpu}")
+    print("| workload | batch | rows per item | blocks timed | seconds | seconds per block | GFLOP/s |")
+    print("|---|---|---|---|---|---|---|")
+    for name, b, r, n, dt, pb, gf in rows:
+        print(f"| {name} | {b} | {r} | {n} | {dt:.2f} | {pb:.2f} | {gf:.1f} |")
+    c4 = rows[-1]
+    print(f"\nThe 24-block c4 stack would take about {24 * c4[5]:.0f} s (12 x the two blocks timed).")
+
+
 def graph_timing(torch, step, stream, steps):
     """ms per block forward when one block is captured in a HIP graph and replayed
     (outside the main timed region); None if capture is not possible here."""
@@ -369,6 +410,9 @@ def graph_timing(torch, step, stream, steps):
 
 def main():
     args = parse()
+    if args.oracle_sweep:
+        oracle_sweep()
+        return
     if args.traffic_summary:
         from diffusion_transformer_denoiser_amd import synth
         traffic_summary(*args.traffic_summary, synth.CONFIGS["c2"])
