@@ -248,12 +248,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
       offb[s][i] = AB + r * 64 + ((2 * s + hh) ^ ((r >> 2) & 3)) * 16;
     }
   }
+  // reads in the order the k-step's MFMAs first use them (w0 a0 w1 a1 a2 a3 ...; the MFMAs run
+  // over the activation fragments in the outer loop), so the first MFMAs' operands arrive first
   auto ldfrag = [&](int slab, int s, bf16x8* fa, bf16x8* fw) {
     const char* base = smem + (slab % STAGES) * (AB + BB);
 #pragma unroll
-    for (int j = 0; j < FM; ++j) fa[j] = *reinterpret_cast<const bf16x8*>(base + offa[s][j]);
+    for (int j = 0; j < FM; ++j) {
+      if (j < FN) fw[j] = *reinterpret_cast<const bf16x8*>(base + offb[s][j]);
+      fa[j] = *reinterpret_cast<const bf16x8*>(base + offa[s][j]);
+    }
 #pragma unroll
-    for (int i = 0; i < FN; ++i) fw[i] = *reinterpret_cast<const bf16x8*>(base + offb[s][i]);
+    for (int i = FM; i < FN; ++i) fw[i] = *reinterpret_cast<const bf16x8*>(base + offb[s][i]);
   };
 
   f32x16 acc[FN][FM];
@@ -278,15 +283,15 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
     if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
     ldfrag(kt, 1, fa1, fw1);
 #pragma unroll
-    for (int i = 0; i < FN; ++i)
+    for (int j = 0; j < FM; ++j)
 #pragma unroll
-      for (int j = 0; j < FM; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw0[i], fa0[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < FN; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw0[i], fa0[j], acc[i][j], 0, 0, 0);
     // slab kt+1 is resident; the last iteration re-reads its own stage so the wait counts stay exact
     ldfrag(kt + 1 < nk ? kt + 1 : kt, 0, fa0, fw0);
 #pragma unroll
-    for (int i = 0; i < FN; ++i)
+    for (int j = 0; j < FM; ++j)
 #pragma unroll
-      for (int j = 0; j < FM; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw1[i], fa1[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < FN; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw1[i], fa1[j], acc[i][j], 0, 0, 0);
 #if MOSS_GEMM_SCHED
     // issue each k-step's fragment reads early in the other k-step's MFMAs
     sched_interleave<MOSS_GEMM_SCHED, FM + FN, FM * FN>();
