@@ -46,26 +46,38 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the C ABI layer
+# (argument validation, planning, launch sequencing); the device code is built
+# as usual.  Each -fsanitize goes right after -Xarch_host.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer"]
+ASAN_LIB = os.path.join(PKG, "_build_asan", "libmoss_asan.so")
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile every source and link libmoss.so (or, with sanitize, the host-sanitizer copy)."""
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    bdir = os.path.dirname(ASAN_LIB) if sanitize else BUILD
+    out = ASAN_LIB if sanitize else LIB
+    extra = HOST_SANITIZE if sanitize else []
+    os.makedirs(bdir, exist_ok=True)
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(bdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(min(len(cmds), 8)) as ex:
         outs = list(ex.map(_run, cmds))
     if verbose:
         for o in outs:
             if o.strip():
                 print(o)
-    tmp = LIB + ".tmp"
-    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = out + ".tmp"
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *extra, "-o", tmp, *objs])
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

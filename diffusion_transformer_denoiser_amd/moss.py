@@ -14,6 +14,9 @@ import re
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoss.so")
+# A differently built copy of the library (the host-sanitizer build the CPU tests run against) may be
+# named here; the product path loads libmoss.so.
+LIB_PATH = os.environ.get("MOSS_LIBRARY", LIB_PATH)
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "moss.h")
 
 MOSS_OK, MOSS_EINVAL, MOSS_EALIAS, MOSS_EWORKSPACE, MOSS_EDEVICE, MOSS_EHIP = range(6)

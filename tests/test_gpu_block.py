@@ -155,6 +155,23 @@ def test_block_repeats_are_byte_identical():
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
 
 
+def test_block_reads_no_unwritten_scratch():
+    """A workspace full of NaN bytes (0xFF) before the call gives the same output bytes as a
+    zeroed one: no kernel reads scratch the call has not written first."""
+    t = G.torch()
+    geom = synth.smaller(synth.CONFIGS["c0"], batch=2, txt_len=(8, 3))
+    G.say("workspace poisoned with NaN bytes")
+    acts = synth.make_activations(geom, 14)
+    w = synth.make_block_weights(geom, 14, 0, std=STRONG)
+    dims = G.geometry_dims(geom)
+    ws = t.empty(moss.moss_workspace_bytes(dims, 1), dtype=t.uint8, device="cuda")
+    ws.fill_(0)
+    clean = G.host_bits(gpu_forward(geom, acts, w, workspace=ws))
+    ws.fill_(255)
+    poisoned = G.host_bits(gpu_forward(geom, acts, w, workspace=ws))
+    np.testing.assert_array_equal(poisoned, clean)
+
+
 def test_stack_small():
     geom = synth.smaller(synth.CONFIGS["c0"], batch=2, txt_len=(8, 2))
     G.say("stack c0-strong x3")

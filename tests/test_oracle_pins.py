@@ -40,3 +40,20 @@ def test_rounded_mode_close_to_exact():
         assert 1.0 - float(u @ v / np.linalg.norm(u) / np.linalg.norm(v)) < 5e-5, k
     assert np.max(np.abs(a - b)) <= 2.0 ** -7 * np.max(np.abs(a))
     assert not np.array_equal(a, b)
+
+
+def test_acceptance_gate_catches_a_planted_row_error():
+    """The block bar (cosine >= 0.9997, max|err| <= 2e-2 max|ref|) fails on an output whose
+    only fault is one row off by 5%, as the pages' per-step gate must (the encoder page,
+    "Receipt": a planted 5% row error fails even when repeats are identical)."""
+    from . import gpu_util as G
+    geom = P.tiny_geoms()[1]
+    x, txt, lens, cond, ws = P.f64_inputs(geom, seed=8)
+    cos, sin = ob.rope_tables(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, geom.head_dim)
+    ref = ob.block_forward(x, txt, lens, cond, ws[0], cos, sin, geom.eps)
+    G.assert_parity("unchanged", ref.copy(), ref)
+    bad = ref.copy()
+    row = int(np.argmax(np.abs(ref).max(axis=-1).ravel()))
+    bad.reshape(-1, ref.shape[-1])[row] *= 1.05
+    with pytest.raises(AssertionError):
+        G.assert_parity("one row 5% off", bad, ref)
