@@ -12,7 +12,8 @@
 //
 //  * Keys advance 64 at a time through two LDS stages (K rows, and V
 //    transposed as the q/k kernel packs it), each filled straight from
-//    global memory with global_load_lds_dwordx4 one tile ahead.  The K chunk
+//    global memory with global_load_lds_dwordx4 one tile ahead (issued from
+//    asm, so the compiler's waits on the fragment reads stay exact).  The K chunk
 //    c of key row r is stored at c ^ (r & 15) (256-byte rows) and the V
 //    chunk c of dim row d at c ^ ((d >> 1) & 7) (128-byte rows), so the 16
 //    rows a 16-lane group reads fall in distinct 16-byte bank slots.
@@ -108,16 +109,15 @@ __global__ __launch_bounds__(kThreads, 8 / NWV) void attn_fwd_kernel(const uint1
     const int dim = blk * 8 + (lane >> 3);
     voff[i] = dim * 64 + (((lane & 7) ^ ((dim >> 1) & 7)) * 8);
   }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(MOSS_LDS char*)smem + 1024u * __builtin_amdgcn_readfirstlane(wave);
   auto issue = [&](int kt) {
-    MOSS_LDS char* base = (MOSS_LDS char*)smem + (kt & 1) * kStage;
     const uint16_t* ks = kb + (size_t)kt * BKV * 128;
     const uint16_t* vs = vb + (size_t)kt * BKV * 128;
+    const uint32_t base = lds0 + (uint32_t)((kt & 1) * kStage);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      __builtin_amdgcn_global_load_lds((const void*)(ks + koff[i]), (MOSS_LDS void*)(base + 1024 * (wave + NWV * i)),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vs + voff[i]),
-                                       (MOSS_LDS void*)(base + 16384 + 1024 * (wave + NWV * i)), 16, 0, 0);
+      dma16(ks + koff[i], base + 1024u * NWV * i);
+      dma16(vs + voff[i], base + 16384u + 1024u * NWV * i);
     }
   };
   // this lane's fragment offsets within a stage

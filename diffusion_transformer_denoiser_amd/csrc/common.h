@@ -62,6 +62,17 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// One 16-byte-per-lane load from global memory straight into LDS: lane l's
+// bytes land at LDS address lds + 16 l (lds wave-uniform, set through M0).
+// Issued from asm, the compiler's wait-count tracking does not see it, so
+// its waits on LDS fragment reads stay exact (while a direct load it knows
+// of is pending, it waits for every outstanding LDS operation).  Callers
+// wait for these loads themselves (s_waitcnt vmcnt) before the barrier that
+// publishes the data.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory");
+}
+
 // Per-launch batch metadata passed by value (txt_len lives on the host).
 struct ItemLens {
   int32_t len[MOSS_MAX_BATCH];

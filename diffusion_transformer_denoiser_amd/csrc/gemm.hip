@@ -6,14 +6,17 @@
 // with v_mfma_f32_32x32x16_bf16; each wavefront owns a (256/WM) x (BN/WN)
 // sub-tile whose fp32 accumulators stay in registers for the whole K loop.
 //
-//  * K advances 32 at a time through a ring of four LDS stages.  Each slab is
-//    fetched straight into LDS with global_load_lds_dwordx4 three slabs ahead
-//    of its use, so no register staging or LDS store instruction is needed.
+//  * K advances 32 at a time through a ring of LDS stages (five, 160 KiB, for
+//    the 256 x 256 tiles).  Each slab is fetched straight into LDS with
+//    global_load_lds_dwordx4 (issued from asm, see dma16) STAGES - 1 slabs
+//    ahead of its use, so no register staging or LDS store instruction is
+//    needed; five stages rather than four gave the loads one more slab to
+//    land (+0.6% per block).
 //  * The MFMA operands of a slab are read from LDS into registers one k-step
 //    ahead, across the slab boundary: when a wavefront reaches the barrier
 //    that ends slab kt, the fragments of slab kt+1 are already in flight, and
 //    slab kt+2 must be resident.  The barrier is a plain s_barrier after an
-//    explicit vmcnt wait that leaves the newest slab's loads outstanding.
+//    explicit vmcnt wait that leaves the newer slabs' loads outstanding.
 //  * A slab row is 64 bytes (32 bf16 of k).  The 16-byte chunk c of row r is
 //    stored at c ^ ((r >> 2) & 3), so the 16 rows a 16-lane group reads for
 //    one operand fragment land in 16 distinct 16-byte slots of the LDS banks.
@@ -222,16 +225,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
     }
     gb[i] = w + (size_t)wrow * ldw + ((lane & 3) ^ ((r >> 2) & 3)) * 8;
   }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(MOSS_LDS char*)smem + 1024u * __builtin_amdgcn_readfirstlane(wave);
   auto issue = [&](int slab) {
-    MOSS_LDS char* base = (MOSS_LDS char*)smem + (slab % STAGES) * (AB + BB);
+    const uint32_t base = lds0 + (uint32_t)((slab % STAGES) * (AB + BB));
 #pragma unroll
-    for (int i = 0; i < LA; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(ga[i] + slab * KB),
-                                       (MOSS_LDS void*)(base + 1024 * (wave + NW * i)), 16, 0, 0);
+    for (int i = 0; i < LA; ++i) dma16(ga[i] + slab * KB, base + 1024u * NW * i);
 #pragma unroll
-    for (int i = 0; i < LB; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(gb[i] + slab * KB),
-                                       (MOSS_LDS void*)(base + AB + 1024 * (wave + NW * i)), 16, 0, 0);
+    for (int i = 0; i < LB; ++i) dma16(gb[i] + slab * KB, base + AB + 1024u * NW * i);
   };
   // byte offsets of this lane's fragments within a stage, for the two k16 steps of a slab
   int offa[2][FM], offb[2][FN];
@@ -334,8 +334,8 @@ hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_
       split = whole + tail * std::ceil((double)nt / cus) < all;
     }
     const int m_main = split ? full * 256 : m;
-    hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI>), dim3(((m_main + 255) / 256) * nt), dim3(512), 0, st, a,
-                       lda, w, ldw, c, ldc, 0, m_main, n, k, ep);
+    hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI, 5>), dim3(((m_main + 255) / 256) * nt), dim3(512), 0, st,
+                       a, lda, w, ldw, c, ldc, 0, m_main, n, k, ep);
     if (split) {
       if (rem <= 64)
         hipLaunchKernelGGL((gemm_nt_kernel<64, 256, 1, 4, EPI>), dim3(nt), dim3(256), 0, st, a, lda, w, ldw, c,
