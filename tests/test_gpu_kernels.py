@@ -105,6 +105,10 @@ def test_mod_rmsnorm(batch, rows, d):
     # 64- / 128-row tail launch after the whole tiles (on a 256-CU device)
     (1058, 16384, 256),
     (1124, 16384, 256),
+    # a last round of 256 x 256 tiles less than half full: its columns run as 128-row tiles
+    # after the whole rounds (the 4096+34-row QKV: 30 + 6 column tiles; 1280 rows: 51 + 9)
+    (4130, 9216, 3072),
+    (1280, 15360, 256),
 ])
 def test_gemm_nt(m, n, k):
     G.say(f"gemm_nt M={m} N={n} K={k}")
@@ -132,6 +136,24 @@ def test_gemm_strided():
     G.sync()
     ref = ob.widen_bf16(a[:, :k]) @ ob.widen_bf16(w[:, :k]).T
     got = G.host_f64(c)
+    G.assert_ulps("c", got[:, :n], ref, ulps=1.0, abs_floor=1e-4)
+    assert np.all(got[:, n:] == 0)
+
+
+def test_gemm_column_split_strided():
+    """The column split with row strides wider than the operands: the second
+    launch's weight and output pointers start nt1 * 256 columns in."""
+    m, n, k = 1280, 15360, 256
+    a = synth.make_tensor(5, 2, (m, 2 * k))
+    w = synth.make_tensor(5, 3, (n, k + 64), std=0.02)
+    c = G.empty_bf16(m, n + 128)
+    c.zero_()
+    G.say("gemm_nt column split, strided")
+    moss.moss_k_gemm_nt(m, n, k, G.dev(a), 2 * k, G.dev(w), k + 64, c, n + 128)
+    G.sync()
+    rows = np.unique(np.r_[0:32, m - 32:m, np.linspace(0, m - 1, 64).astype(int)])
+    ref = ob.widen_bf16(a[rows, :k]) @ ob.widen_bf16(w[:, :k]).T
+    got = G.host_f64(c)[rows]
     G.assert_ulps("c", got[:, :n], ref, ulps=1.0, abs_floor=1e-4)
     assert np.all(got[:, n:] == 0)
 
