@@ -213,8 +213,9 @@ def cpu_baseline(geom, acts, wbits):
                       f"{threads} host cores)"}
 
 
-# the steps that launch kernels of their own (the gated adds and the SiLU product run in GEMM epilogues)
-PROBED = ("JOIN", "ADALN", "NORM1", "QKV", "QKNORM", "ATTN", "OUT", "NORM2", "UP", "DOWN")
+# the steps that launch kernels of their own (the q/k norm and packing, the gated adds and the SiLU
+# product run in GEMM epilogues)
+PROBED = ("JOIN", "ADALN", "NORM1", "QKV", "ATTN", "OUT", "NORM2", "UP", "DOWN")
 # algorithmic work per step at one block forward of this workload: (GFLOP, MB)
 def step_work(geom):
     m, d, f = geom.batch * geom.rows, geom.d_model, geom.mlp_inner
@@ -225,7 +226,6 @@ def step_work(geom):
         "ADALN": (2 * geom.batch * 6 * d * d / 1e9, 2 * 6 * d * d / 1e6),
         "NORM1": (0.0, (4 * m * d + 2 * m * d) / 1e6),
         "QKV": (2 * m * 3 * d * d / 1e9, None),
-        "QKNORM": (0.0, (2 * m * 3 * d + 2 * 3 * geom.batch * geom.n_heads * ((t + 127) // 128 * 128) * 128) / 1e6),
         "ATTN": (4 * geom.batch * geom.n_heads * t * t * 128 / 1e9, None),
         "OUT": (2 * m * d * d / 1e9, None),
         "NORM2": (0.0, (4 * m * d + 2 * m * d) / 1e6),

@@ -6,14 +6,21 @@
 // gfx950 design.  A workgroup owns 256 queries of one (item, head); each of
 // its eight wavefronts owns 32 queries and keeps them in registers as MFMA
 // operands for the whole key loop.  One workgroup fills a CU (2 wavefronts
-// per SIMD), so one wavefront's softmax overlaps the other's MFMAs, and each
-// K/V tile is loaded into LDS once for 256 queries (a 128-query workgroup,
-// two per CU, loaded every tile twice per CU and ran 1% slower overall).
+// per SIMD), and each K/V tile is loaded into LDS once for 256 queries (a
+// 128-query workgroup, two per CU, loaded every tile twice per CU and ran 1%
+// slower overall).
 //
-//  * Keys advance 64 at a time through two LDS stages (K rows, and V
-//    transposed as the q/k kernel packs it), each filled straight from
-//    global memory with global_load_lds_dwordx4 one tile ahead (issued from
-//    asm, so the compiler's waits on the fragment reads stay exact).  The K chunk
+//  * The two wavefronts of a SIMD work a phase apart (wavefronts 0-3 and 4-7
+//    form two groups, one of each per SIMD).  A wavefront alternates a
+//    matrix step (O^T += V^T P^T for the previous tile, then S^T = K Q^T for
+//    this one) with a softmax step, so one group's softmax can issue while
+//    the other group's MFMAs occupy the SIMD's matrix pipe.  With one phase
+//    for both (the earlier form), both wavefronts of a SIMD ran their MFMAs,
+//    then both their softmax, and the two pipes seldom overlapped.
+//  * Keys advance 64 at a time through three LDS stages (K rows, and the 64-key
+//    V^T tile: 128 dim rows of 64 keys), each filled straight from
+//    global memory with global_load_lds_dwordx4 (issued from asm, so the
+//    compiler's waits on the fragment reads stay exact).  The K chunk
 //    c of key row r is stored at c ^ (r & 15) (256-byte rows) and the V
 //    chunk c of dim row d at c ^ ((d >> 1) & 7) (128-byte rows), so the 16
 //    rows a 16-lane group reads fall in distinct 16-byte bank slots.
@@ -34,9 +41,11 @@
 //    then probabilities may reach 2^8, which fp32 sums and bf16 products hold
 //    exactly as well, and O and the sum need no rescale.
 //  * The probabilities, rounded to bf16, are already laid out as the second
-//    operand of O^T += V^T P^T (the packed V stores the keys of each 16-key
-//    group in the order a lane holds its scores).  O^T stays in 64
-//    accumulators per lane; no probability goes through LDS.
+//    operand of O^T += V^T P^T: the K fragments read their key rows with
+//    quads 1 and 2 of each 16-key group swapped, so each lane holds the
+//    scores of 8 consecutive keys per group, the keys one 16-byte read of a
+//    V^T row gives.  O^T stays in 64 accumulators per lane; no probability
+//    goes through LDS.
 // Keys that are text padding (txt_len <= key < n_txt) or past the last row
 // get -inf; a tile with no valid key leaves the state as it is.
 #include <math.h>
@@ -46,21 +55,33 @@
 
 namespace {
 
-// V fragment reads issued ahead of the PV MFMAs (0: the compiler's own order)
+// fragment reads issued ahead of the MFMAs of a matrix step (0: the compiler's own order)
 #ifndef MOSS_ATTN_SCHED
 #define MOSS_ATTN_SCHED 4
 #endif
 
-#ifndef MOSS_ATTN_WAVES
-#define MOSS_ATTN_WAVES 8
-#endif
-constexpr int NWV = MOSS_ATTN_WAVES;  // wavefronts per workgroup, 32 queries each
-constexpr int BQ = 32 * NWV;         // queries per workgroup
-constexpr int LPW = 16 / NWV;        // 1 KiB direct loads per wavefront per K (and per V) tile
-constexpr int BKV = 64;  // keys per tile
+constexpr int NWV = 8;           // wavefronts per workgroup, 32 queries each: two groups of four
+constexpr int BQ = 32 * NWV;     // queries per workgroup
+constexpr int LPW = 16 / NWV;    // 1 KiB direct loads per wavefront per K (and per V) tile
+constexpr int BKV = 64;          // keys per tile
 constexpr int kThreads = 64 * NWV;
-constexpr int kStage = 32768;  // K tile (16 KiB) then V^T tile (16 KiB)
+constexpr int kStage = 32768;    // K tile (16 KiB) then V^T tile (16 KiB)
+constexpr int kStages = 3;       // K/V tiles in LDS
+#ifndef MOSS_ATTN_MSUM
+#define MOSS_ATTN_MSUM 0
+#endif
 constexpr float kLazy = 8.0f;  // log2-unit growth of a row max that forces a rescale
+
+// Row r of a 32-key block of S^T holds key quad_swap(r): quads 1 and 2 of
+// each 16-key group trade places (the K fragment's lane l32 reads key row
+// quad_swap(l32)).  A lane then holds, for each 16-key group, the scores of
+// 8 consecutive keys (4hh..4hh+3 and 8+4hh..11+4hh of S^T's rows are keys
+// 8hh..8hh+7), which is what the V^T fragment of the PV product pairs with:
+// 8 consecutive keys of one dim, one 16-byte read from a plain V^T tile.
+__device__ __forceinline__ int quad_swap(int r) {
+  const int q = (r >> 2) & 3;
+  return (r & ~15) | ((q == 1 ? 2 : (q == 2 ? 1 : q)) << 2) | (r & 3);
+}
 
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -71,13 +92,13 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__global__ __launch_bounds__(kThreads, 8 / NWV) void attn_fwd_kernel(const uint16_t* __restrict__ qp,
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const uint16_t* __restrict__ qp,
                                                                const uint16_t* __restrict__ kp,
                                                                const uint16_t* __restrict__ vp,
                                                                uint16_t* __restrict__ o, int rows, int rows_pad,
                                                                int n_heads, int n_txt, ItemLens lens,
                                                                float scale_log2) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStage];
 
   const int qt = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
@@ -113,7 +134,7 @@ __global__ __launch_bounds__(kThreads, 8 / NWV) void attn_fwd_kernel(const uint1
   auto issue = [&](int kt) {
     const uint16_t* ks = kb + (size_t)kt * BKV * 128;
     const uint16_t* vs = vb + (size_t)kt * BKV * 128;
-    const uint32_t base = lds0 + (uint32_t)((kt & 1) * kStage);
+    const uint32_t base = lds0 + (uint32_t)((kt % kStages) * kStage);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       dma16(ks + koff[i], base + 1024u * NWV * i);
@@ -124,7 +145,7 @@ __global__ __launch_bounds__(kThreads, 8 / NWV) void attn_fwd_kernel(const uint1
   int kfo[2][8], vfo[4][4];
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
-    const int key = h2 * 32 + l32;
+    const int key = h2 * 32 + quad_swap(l32);
 #pragma unroll
     for (int s = 0; s < 8; ++s) kfo[h2][s] = key * 256 + (((2 * s + hh) ^ (key & 15)) * 16);
   }
@@ -142,25 +163,40 @@ __global__ __launch_bounds__(kThreads, 8 / NWV) void attn_fwd_kernel(const uint1
     for (int e = 0; e < 16; ++e) acc_o[i][e] = 0.0f;
   float m_use = -INFINITY;  // max (log2 units, scaled) the exponentials are taken against
   float l_run = 0.0f;
+#if MOSS_ATTN_MSUM
+  // The row sums of the probabilities come out of the PV product: a first
+  // operand whose row 0 is all ones gives, in row 0 of its accumulator, the
+  // sum over the tile's keys of each query's bf16 probabilities (lanes 0-31
+  // hold row 0; the other rows stay zero).
+  f32x16 acc_l;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc_l[e] = 0.0f;
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)(l32 == 0 ? 1.0f : 0.0f);
+#endif
 
   const int n_tiles = (rows + BKV - 1) / BKV;
+  // Phase 2t is group 0's matrix step t and phase 2t+1 its softmax of tile
+  // t; group 1 runs one phase behind.  Tile t's K is read in phases 2t and
+  // 2t+1 and its V^T in 2t+2 and 2t+3, so three stages rotate: tile t+2 is
+  // loaded after the barrier that ends phase 2t+1 (into the stage of tile
+  // t-1, whose last reads were in that phase) and waited for at the barrier
+  // that ends phase 2t+3.  Only those barriers are workgroup barriers; the
+  // offset between the groups comes from the program order alone (a second
+  // barrier per tile, to pin it, cost 1% per block).
+  const int grp = wave >> 2;
+  f32x16 sacc[2];
+  bf16x8 pf[4];
   issue(0);
-  // The query fragments pass through this statement, so the compiler treats
-  // them as ready here and the loop's MFMAs never wait on the vector memory
-  // counter (which the tile loads also count) for them.
+  if (n_tiles > 1) issue(1);
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier"
                : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]), "+v"(qf[4]), "+v"(qf[5]), "+v"(qf[6]),
                  "+v"(qf[7])
                :
                : "memory");
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    // stage (kt+1)&1 held tile kt-1, whose reads finished before the previous barrier
-    if (kt + 1 < n_tiles) issue(kt + 1);
-    const char* st = smem + (kt & 1) * kStage;
-
-    // S^T for keys 0-31 (h2 = 0) and 32-63 (h2 = 1): the two accumulator
-    // chains alternate so no MFMA waits on the one just issued
-    f32x16 sacc[2];
+  auto qk = [&](int t) {
+    const char* st = smem + (t % kStages) * kStage;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -174,25 +210,31 @@ __global__ __launch_bounds__(kThreads, 8 / NWV) void attn_fwd_kernel(const uint1
     for (int s = 0; s < 8; ++s)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s][h2], qf[s], sacc[h2], 0, 0, 0);
-#if MOSS_ATTN_SCHED
-    // K fragment reads run 4 ahead of the MFMAs that use them
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  };
+  auto pv = [&](int t) {
+    const char* st = smem + (t % kStages) * kStage;
+    bf16x8 vf[4][4];
 #pragma unroll
-    for (int q = 0; q < 12; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vf[s][i] = *reinterpret_cast<const bf16x8*>(st + vfo[i][s]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc_o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s][i], pf[s], acc_o[i], 0, 0, 0);
+#if MOSS_ATTN_MSUM
+      acc_l = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[s], acc_l, 0, 0, 0);
 #endif
-
-    // lane holds keys 32*h2 + 8*q + 4*hh + e at sacc[h2][4q + e]
-    const int key0 = kt * BKV;
+    }
+  };
+  auto softmax = [&](int t) {
+    const int key0 = t * BKV;
     if ((key0 + BKV > rows) || (key0 < n_txt && key0 + BKV > valid_txt)) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = key0 + h2 * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+          const int key = key0 + h2 * 32 + quad_swap(8 * (e >> 2) + 4 * hh + (e & 3));
           const bool bad = (key >= rows) || (key >= valid_txt && key < n_txt);
           sacc[h2][e] = bad ? -INFINITY : sacc[h2][e];
         }
@@ -203,11 +245,14 @@ __global__ __launch_bounds__(kThreads, 8 / NWV) void attn_fwd_kernel(const uint1
 #pragma unroll
       for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[h2][e]);
     mloc = pair_max(mloc) * scale_log2;
-    // move the reference max (for every row of the wavefront at once) only when some row grew a lot
     if (__builtin_amdgcn_ballot_w64(mloc > m_use + kLazy) != 0ull) {
       const float m_new = fmaxf(m_use, mloc);
-      const float corr = __builtin_amdgcn_exp2f(m_use - m_new);  // 0 on the first valid tile
+      const float corr = __builtin_amdgcn_exp2f(m_use - m_new);
+#if MOSS_ATTN_MSUM
+      acc_l[0] *= corr;
+#else
       l_run *= corr;
+#endif
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -215,43 +260,81 @@ __global__ __launch_bounds__(kThreads, 8 / NWV) void attn_fwd_kernel(const uint1
       m_use = m_new;
     }
     const float moff = (m_use == -INFINITY) ? 0.0f : m_use;
+#if !MOSS_ATTN_MSUM
     float lsum = 0.0f;
-    bf16x8 pf[4];
+#endif
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[h2][8 * half + t], scale_log2, -moff));
+        for (int tt = 0; tt < 8; ++tt) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[h2][8 * half + tt], scale_log2, -moff));
+#if !MOSS_ATTN_MSUM
           lsum += p;
-          pf[2 * h2 + half][t] = (__bf16)p;
+#endif
+          pf[2 * h2 + half][tt] = (__bf16)p;
         }
+#if !MOSS_ATTN_MSUM
     l_run += pair_sum(lsum);
-
-    // O^T += V^T P^T over four 16-key steps; the four accumulators alternate
-    bf16x8 vf[4][4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vf[s][i] = *reinterpret_cast<const bf16x8*>(st + vfo[i][s]);
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc_o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s][i], pf[s], acc_o[i], 0, 0, 0);
+#endif
+  };
+  // ends of the even phases: nothing is scheduled across them
+  auto bar = [&]() { __builtin_amdgcn_sched_barrier(0); };
+  // end of phase 2t+1: tile t+1 (loaded after the previous such barrier) must be resident; then
+  // tile t+2 goes into the stage of tile t-1
+  auto bar_load = [&](int t) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t + 2 < n_tiles) issue(t + 2);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // a matrix step: O^T += V^T P^T for tile t-1, then S^T = K Q^T for tile t
+  auto pv_qk = [&](int t) {
+    pv(t - 1);
+    qk(t);
 #if MOSS_ATTN_SCHED
-    __builtin_amdgcn_sched_group_barrier(0x100, MOSS_ATTN_SCHED, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int q = 0; q < 16 - MOSS_ATTN_SCHED; ++q) {
+    for (int q = 0; q < 28; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, MOSS_ATTN_SCHED, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 #endif
-
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  // Both groups pass the same n_tiles + 1 workgroup barriers (the first one above).
+  if (__builtin_amdgcn_readfirstlane(grp) == 0) {
+    qk(0);
+    bar();
+    for (int t = 0; t + 1 < n_tiles; ++t) {
+      softmax(t);
+      bar_load(t);
+      pv_qk(t + 1);
+      bar();
+    }
+    softmax(n_tiles - 1);
+    bar_load(n_tiles - 1);
+    pv(n_tiles - 1);
+    bar();
+  } else {
+    bar();
+    qk(0);
+    bar_load(0);
+    softmax(0);
+    bar();
+    for (int t = 1; t < n_tiles; ++t) {
+      pv_qk(t);
+      bar_load(t);
+      softmax(t);
+      bar();
+    }
+    pv(n_tiles - 1);
   }
 
+#if MOSS_ATTN_MSUM
+  l_run = pair_sum(acc_l[0]);
+#endif
   // acc_o[i][4q + e] = O^T[dim = 32 i + 8 q + 4 hh + e][query l32]
   if (qrow < rows) {
     const float inv = 1.0f / l_run;

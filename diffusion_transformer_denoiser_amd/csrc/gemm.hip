@@ -52,14 +52,25 @@ namespace {
 
 constexpr int KB = 32;      // k per slab
 
-enum Epi { kStore = 0, kSiluGate = 1, kGatedAdd = 2 };
+enum Epi { kStore = 0, kSiluGate = 1, kGatedAdd = 2, kQkvPack = 3 };
 
 struct EpiArgs {
   float* h;           // kGatedAdd: fp32 residual [m, n], row stride n
   const float* gate;  // kGatedAdd: gate of item b at gate + b * gate_stride
   int gate_stride;
-  int rows_per_item;
+  int rows_per_item;  // kGatedAdd, kQkvPack: rows of one item
   uint16_t* out16;    // kGatedAdd: when set, bf16 result here instead of updating h
+  // kQkvPack: q/k gains [128], the rotary table re-laid as pairs of pairs (launch_rope_pairs:
+  // rope_pp[cs][pp][t][2] = rope[cs][t][2 pp + 0/1], cs 0 cos / 1 sin, row stride rows_pad), packed outputs
+  const uint16_t* q_gain;
+  const uint16_t* k_gain;
+  const float* rope_pp;
+  uint16_t* qo;
+  uint16_t* ko;
+  uint16_t* vo;
+  int rows_pad, n_heads;
+  float eps;
+  int col0;           // kQkvPack: absolute column of this launch's column 0
 };
 
 #ifndef MOSS_GEMM_GROUP
@@ -175,6 +186,126 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[BN / WN / 32][BM / 
           *reinterpret_cast<u32x2*>(crow + col) = v;
         }
       }
+    }
+  }
+}
+
+// kQkvPack: the QKV projection with a4 in its epilogue.  Each value is first
+// rounded to bf16, as the projection output would store it.  A wavefront owns
+// 64 columns, half of one head of q, k or v; for q and k the per-(row, head)
+// sum of squares adds the partner wavefront's half through LDS, then each
+// value is scaled by 1/sqrt(mean + eps) and the gain and its pair rotated,
+// and the row goes to the packed Q or K layout [B, H, T_pad, 128].  v values
+// go to V^T [B, H, T_pad/64, 128, 64] one bf16 at a time (the 32 lanes of a
+// half wavefront write 32 consecutive keys of one dim: one 64-byte segment).
+#ifndef MOSS_QKV_SS_ROUNDED
+#define MOSS_QKV_SS_ROUNDED 1
+#endif
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void epilogue_qkv(const f32x16 (&acc)[BN / WN / 32][BM / WM / 32], char* smem, int m0,
+                                             int n0, int wave, int wm, int wn, int l32, int hh, int m,
+                                             const EpiArgs& ep) {
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  static_assert(TN == 64 && FN == 2 && WN % 2 == 0, "a head's 128 columns are one pair of wavefronts");
+  const int T = ep.rows_per_item, H = ep.n_heads, D = H * 128;
+  const int col = ep.col0 + n0 + wn * TN;  // this wavefront's first column of [q | k | v]
+  const int which = col / D, head = (col - which * D) >> 7, half = ((col - which * D) >> 6) & 1;
+
+  // the value as the projection output would store it, rounded where used rather than kept (the
+  // sums of squares round with integer arithmetic, to the same nearest-even bf16 for finite values,
+  // so the compiler does not keep those results live across the barrier for the second use)
+  auto xr = [&](int i, int j, int e) { return (float)(__bf16)acc[i][j][e]; };
+  auto xr_int = [&](int i, int j, int e) {
+    const uint32_t u = __float_as_uint(acc[i][j][e]);
+    return __uint_as_float((u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u);
+  };
+  float ss[FM];
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    float sj = 0.0f;
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+#if MOSS_QKV_SS_ROUNDED
+        const float v = xr_int(i, j, e);
+#else
+        const float v = acc[i][j][e];
+#endif
+        sj += v * v;
+      }
+    ss[j] = sj + __shfl_xor(sj, 32, 64);  // the wavefront's 64 columns of row j*32 + l32
+  }
+  float* ss_lds = reinterpret_cast<float*>(smem);  // [wavefront][TM]; the K loop's last reads are done
+  if (hh == 0)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) ss_lds[wave * TM + j * 32 + l32] = ss[j];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < FM; ++j) ss[j] += ss_lds[(wave ^ 1) * TM + j * 32 + l32];
+
+  if (which < 2) {
+    // gains of this lane's dims half*64 + 32 i + 8 q + 4 hh + e
+    float g[FN][4][4];
+    const uint16_t* gsrc = (which ? ep.k_gain : ep.q_gain) + half * 64 + 4 * hh;
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x2 w2 = *reinterpret_cast<const u32x2*>(gsrc + i * 32 + 8 * q);
+        g[i][q][0] = bf16_lo(w2[0]);
+        g[i][q][1] = bf16_hi(w2[0]);
+        g[i][q][2] = bf16_lo(w2[1]);
+        g[i][q][3] = bf16_hi(w2[1]);
+      }
+    uint16_t* dbase = which ? ep.ko : ep.qo;
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int row = m0 + wm * TM + j * 32 + l32;
+      if (row >= m) continue;
+      const int b = row / T, t = row - b * T;
+      const float r = 1.0f / sqrtf(ss[j] / 128.0f + ep.eps);
+      // pair p0 = half*32 + 16 i + 4 q + 2 hh and p0 + 1: one float2 of the pair-of-pairs table per (i, q);
+      // the 32 lanes of a half wavefront read 32 consecutive rows of it, 256 contiguous bytes
+      const float* cr = ep.rope_pp + ((size_t)(half * 16 + hh) * ep.rows_pad + t) * 2;
+      const float* sr = cr + (size_t)32 * ep.rows_pad * 2;
+      uint16_t* dst = dbase + (((size_t)b * H + head) * ep.rows_pad + t) * 128 + half * 64 + 4 * hh;
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const size_t po = (size_t)(8 * i + 2 * q) * ep.rows_pad * 2;  // pair-of-pairs p0 / 2 - (half*16 + hh)
+          const float2 c2 = *reinterpret_cast<const float2*>(cr + po);
+          const float2 s2 = *reinterpret_cast<const float2*>(sr + po);
+          const float cs[2] = {c2.x, c2.y}, sn[2] = {s2.x, s2.y};
+          float o[4];
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const float x0 = (xr(i, j, 4 * q + 2 * pr) * r) * g[i][q][2 * pr];
+            const float x1 = (xr(i, j, 4 * q + 2 * pr + 1) * r) * g[i][q][2 * pr + 1];
+            o[2 * pr] = x0 * cs[pr] - x1 * sn[pr];
+            o[2 * pr + 1] = x0 * sn[pr] + x1 * cs[pr];
+          }
+          u32x2 v = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          *reinterpret_cast<u32x2*>(dst + i * 32 + 8 * q) = v;
+        }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int row = m0 + wm * TM + j * 32 + l32;
+      if (row >= m) continue;
+      const int b = row / T, t = row - b * T;
+      uint16_t* dst = ep.vo + ((((size_t)b * H + head) * (ep.rows_pad / 64) + t / 64) * 128 + half * 64 + 4 * hh) * 64 +
+                      (t & 63);
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            dst[(i * 32 + 8 * q + e) * 64] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][4 * q + e]);
     }
   }
 }
@@ -301,7 +432,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
     wait_slabs_barrier<PER, STAGES - 3>(min(nk - 1, kt + STAGES - 1) - (kt + 2));
   }
 
-  epilogue<BM, BN, WM, WN, EPI>(acc, m0, n0, tn, wm, wn, l32, hh, m, n, c, ldc, ep);
+  if constexpr (EPI == kQkvPack)
+    epilogue_qkv<BM, BN, WM, WN>(acc, smem, m0, n0, wave, wm, wn, l32, hh, m, ep);
+  else
+    epilogue<BM, BN, WM, WN, EPI>(acc, m0, n0, tn, wm, wn, l32, hh, m, n, c, ldc, ep);
 }
 
 int cu_count() {
@@ -335,7 +469,7 @@ hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_
       const double whole = std::ceil((double)full * nt / cus), all = std::ceil((double)(full + 1) * nt / cus);
       split = whole + tail * std::ceil((double)nt / cus) < all;
     }
-    if (!split && EPI == kStore) {
+    if (!split && (EPI == kStore || EPI == kQkvPack)) {
       // When the 256 x 256 tiles leave a last round less than half full, the
       // whole rounds take the first column tiles and the remaining columns
       // run as 128-row tiles: one round again, but about half as deep.
@@ -344,8 +478,11 @@ hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_
       if (rounds >= 1 && left > 0 && 2 * left <= cus && nt1 > 0 && nt2 > 0 && mt2 * nt2 <= cus) {
         hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI, 5>), dim3(mt * nt1), dim3(512), 0, st, a, lda, w, ldw,
                            c, ldc, 0, m, nt1 * 256, k, ep);
+        EpiArgs ep2 = ep;
+        ep2.col0 = ep.col0 + nt1 * 256;
         hipLaunchKernelGGL((gemm_nt_kernel<128, 256, 2, 4, EPI>), dim3(mt2 * nt2), dim3(512), 0, st, a, lda,
-                           w + (size_t)nt1 * 256 * ldw, ldw, c + (size_t)nt1 * 256, ldc, 0, m, nt2 * 256, k, ep);
+                           w + (size_t)nt1 * 256 * ldw, ldw, c ? c + (size_t)nt1 * 256 : c, ldc, 0, m, nt2 * 256, k,
+                           ep2);
         return hipGetLastError();
       }
     }
@@ -375,6 +512,25 @@ hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_
 hipError_t launch_gemm_nt(int m, int n, int k, const uint16_t* a, int lda, const uint16_t* w, int ldw,
                           uint16_t* c, int ldc, hipStream_t st) {
   return launch<kStore>(m, n, k, a, lda, w, ldw, c, ldc, EpiArgs{}, st);
+}
+
+hipError_t launch_gemm_qkv_pack(int batch, int rows, int n_heads, float eps, const uint16_t* a, const uint16_t* w_qkv,
+                                const uint16_t* q_gain, const uint16_t* k_gain, const float* rope_pp, uint16_t* q,
+                                uint16_t* k, uint16_t* v, hipStream_t st) {
+  const int d = n_heads * 128;
+  EpiArgs ep{};
+  ep.rows_per_item = rows;
+  ep.q_gain = q_gain;
+  ep.k_gain = k_gain;
+  ep.rope_pp = rope_pp;
+  ep.qo = q;
+  ep.ko = k;
+  ep.vo = v;
+  ep.rows_pad = packed_rows(rows);
+  ep.n_heads = n_heads;
+  ep.eps = eps;
+  ep.col0 = 0;
+  return launch<kQkvPack>(batch * rows, 3 * d, d, a, d, w_qkv, d, nullptr, 3 * d, ep, st);
 }
 
 hipError_t launch_gemm_silu(int m, int f, int k, const uint16_t* a, int lda, const uint16_t* w_up, int ldw,

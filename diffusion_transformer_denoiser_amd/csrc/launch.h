@@ -46,6 +46,18 @@ hipError_t launch_gemm_gated_add(int m, int n, int k, const uint16_t* a, int lda
 // Rows of the packed attention layouts: rows rounded up to a multiple of 128.
 inline int packed_rows(int rows) { return (rows + 127) / 128 * 128; }
 
+// The rotary table [2][rows][64] re-laid as pairs of pairs: rope_pp[cs][pp][t][2] =
+// rope[cs][t][2 pp + 0/1] (32 pp, t < rows, row stride packed_rows(rows)); 512 packed_rows(rows) bytes.
+hipError_t launch_rope_pairs(const float* rope, int rows, float* rope_pp, hipStream_t st);
+// The QKV projection of a [batch * rows, 128 n_heads] with a4 in its epilogue: packed Q and K
+// [B, H, T_pad, 128] (normed, gained, rotated with rope_pp from launch_rope_pairs) and V^T
+// [B, H, T_pad/64, 128, 64]; pad rows untouched.
+hipError_t launch_gemm_qkv_pack(int batch, int rows, int n_heads, float eps, const uint16_t* a, const uint16_t* w_qkv,
+                                const uint16_t* q_gain, const uint16_t* k_gain, const float* rope_pp, uint16_t* q,
+                                uint16_t* k, uint16_t* v, hipStream_t st);
+// Zero the pad rows T..T_pad-1 of packed Q and K and the pad keys of V^T.
+hipError_t launch_zero_packed_pads(int batch, int rows, int n_heads, uint16_t* q, uint16_t* k, uint16_t* v,
+                                   hipStream_t st);
 hipError_t launch_qk_norm_rope_pack(int batch, int rows, int n_heads, float eps, const uint16_t* qkv,
                                     const uint16_t* q_gain, const uint16_t* k_gain, const float* rope,
                                     uint16_t* q, uint16_t* k, uint16_t* v, hipStream_t st);

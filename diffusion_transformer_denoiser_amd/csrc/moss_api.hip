@@ -59,17 +59,19 @@ bool lens_ok(const moss_dims* d, const int32_t* txt_len, ItemLens* out) {
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t s_cond, mod, h, a, qkv, qp, kp, vp, z, total;
+  size_t s_cond, mod, h, a, rope_pp, qp, kp, vp, z, total;
 };
 
 // Offsets (bytes) into the workspace.  h is the fp32 residual stream (the
 // running sum of the gated adds, rounded to bf16 only when `out` is written).
 // a holds the first norm's output, then the attention output, then the second
-// norm's output.  One union region holds the qkv rows and packed q/k/v during
-// attention, and the MLP activation z after.  The projection outputs added to
-// the residual and the up projection's output never reach memory: the out and
-// down projections add into h in their epilogues, and the up projection
-// applies the SiLU gate in its epilogue.
+// norm's output.  rope_pp is the rotary table re-laid for the QKV epilogue
+// (once per call).  qp, kp and vp are the packed Q, K and V^T the QKV
+// projection writes from its epilogue (their pad rows are zeroed once per
+// call and never written again); z is the MLP activation.  No projection
+// output reaches memory as such: QKV is normed, rotated and packed in its
+// epilogue, the out and down projections add into h in theirs, and the up
+// projection applies the SiLU gate in its own.
 Layout plan(const moss_dims* d) {
   Layout L;
   const size_t B = d->batch, T = (size_t)d->n_txt + d->n_img, D = d->d_model, F = d->mlp_inner;
@@ -84,16 +86,13 @@ Layout plan(const moss_dims* d) {
   L.mod = take(4 * B * 6 * D);
   L.h = take(4 * R * D);
   L.a = take(2 * R * D);
-  const size_t base = off;
-  const size_t packed = round256(2 * B * H * Tp * 128);
-  L.qkv = base;
-  L.qp = base + round256(2 * R * 3 * D);
-  L.kp = L.qp + packed;
-  L.vp = L.kp + packed;
-  const size_t end1 = L.vp + packed;
-  L.z = base;
-  const size_t end2 = L.z + round256(2 * R * F);
-  L.total = end1 > end2 ? end1 : end2;
+  const size_t packed = 2 * B * H * Tp * 128;
+  L.rope_pp = take(512 * Tp);
+  L.qp = take(packed);
+  L.kp = take(packed);
+  L.vp = take(packed);
+  L.z = take(2 * R * F);
+  L.total = off;
   return L;
 }
 
@@ -189,7 +188,6 @@ int run_block(const Ctx& c, const moss_block_weights* w, const float* rope, floa
   float* s = reinterpret_cast<float*>(c.ws + c.L.s_cond);
   float* mod = reinterpret_cast<float*>(c.ws + c.L.mod);
   uint16_t* a = reinterpret_cast<uint16_t*>(c.ws + c.L.a);
-  uint16_t* qkv = reinterpret_cast<uint16_t*>(c.ws + c.L.qkv);
   uint16_t* qp = reinterpret_cast<uint16_t*>(c.ws + c.L.qp);
   uint16_t* kp = reinterpret_cast<uint16_t*>(c.ws + c.L.kp);
   uint16_t* vp = reinterpret_cast<uint16_t*>(c.ws + c.L.vp);
@@ -210,13 +208,10 @@ int run_block(const Ctx& c, const moss_block_weights* w, const float* rope, floa
     MOSS_TRY(launch_mod_rmsnorm(h, mod + 0 * D, mod + 1 * D, ms, a, B, T, D, d->eps, st), "mod_rmsnorm");
   }
   {
-    StepTimer t(MOSS_STEP_QKV, st);
-    MOSS_TRY(launch_gemm_nt(R, 3 * D, D, a, D, w->w_qkv, D, qkv, 3 * D, st), "gemm qkv");
-  }
-  {
-    StepTimer t(MOSS_STEP_QKNORM, st);
-    MOSS_TRY(launch_qk_norm_rope_pack(B, T, H, d->eps, qkv, w->q_gain, w->k_gain, rope, qp, kp, vp, st),
-             "qk_norm_rope_pack");
+    StepTimer t(MOSS_STEP_QKV, st);  // QKV projection + q/k norm, rotary and packing
+    MOSS_TRY(launch_gemm_qkv_pack(B, T, H, d->eps, a, w->w_qkv, w->q_gain, w->k_gain,
+                                  reinterpret_cast<const float*>(c.ws + c.L.rope_pp), qp, kp, vp, st),
+             "gemm qkv + pack");
   }
   {
     StepTimer t(MOSS_STEP_ATTN, st);
@@ -294,6 +289,13 @@ int run_stack(const Ctx& c, int n_blocks, const uint16_t* x, const uint16_t* txt
   float* h = reinterpret_cast<float*>(c.ws + c.L.h);
   MOSS_TRY(launch_silu_cond(cond, reinterpret_cast<float*>(c.ws + c.L.s_cond), d->batch, d->d_model, c.st),
            "silu_cond");
+  MOSS_TRY(launch_zero_packed_pads(d->batch, d->n_txt + d->n_img, d->n_heads,
+                                   reinterpret_cast<uint16_t*>(c.ws + c.L.qp),
+                                   reinterpret_cast<uint16_t*>(c.ws + c.L.kp),
+                                   reinterpret_cast<uint16_t*>(c.ws + c.L.vp), c.st),
+           "zero packed pads");
+  MOSS_TRY(launch_rope_pairs(rope, d->n_txt + d->n_img, reinterpret_cast<float*>(c.ws + c.L.rope_pp), c.st),
+           "rope pairs");
   for (int i = 0; i < n_blocks; ++i) {
     unsigned mask = 0;
     if (skip)
@@ -602,6 +604,44 @@ int moss_k_qk_norm_rope_pack(int32_t batch, int32_t rows, int32_t n_heads, float
   if (rc != MOSS_OK) return rc;
   MOSS_TRY(launch_qk_norm_rope_pack(batch, rows, n_heads, eps, qkv, q_gain, k_gain, rope, q, k, v, stream),
            "qk_norm_rope_pack");
+  return MOSS_OK;
+}
+
+int moss_k_gemm_qkv_pack(int32_t batch, int32_t rows, int32_t n_heads, float eps, const uint16_t* a,
+                         const uint16_t* w_qkv, const uint16_t* q_gain, const uint16_t* k_gain, const float* rope,
+                         uint16_t* q, uint16_t* k, uint16_t* v, void* workspace, size_t ws_bytes,
+                         hipStream_t stream) {
+  if (batch < 1 || batch > MOSS_MAX_BATCH || rows < 1 || rows > MOSS_MAX_ROWS || n_heads < 1 ||
+      n_heads * MOSS_HEAD_DIM > MOSS_MAX_DMODEL || !(eps > 0.0f) || !isfinite(eps))
+    return MOSS_EINVAL;
+  const void* p[] = {a, w_qkv, q_gain, k_gain, rope, q, k, v};
+  for (const void* x : p)
+    if (!x || !aligned16(x)) return MOSS_EINVAL;
+  const size_t d = (size_t)n_heads * MOSS_HEAD_DIM;
+  const size_t pk = 2ull * batch * n_heads * packed_rows(rows) * 128;
+  const size_t in = 2ull * batch * rows * d, wb = 2 * 3 * d * d;
+  const void* outs[] = {q, k, v};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(outs[i], pk, a, in) || overlaps(outs[i], pk, w_qkv, wb) || overlaps(outs[i], pk, rope, 8ull * rows * 64))
+      return MOSS_EALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], pk, outs[j], pk)) return MOSS_EALIAS;
+  }
+  if (!workspace || !aligned16(workspace)) return MOSS_EWORKSPACE;
+  const size_t need = 512ull * packed_rows(rows);
+  if (ws_bytes < need) return MOSS_EWORKSPACE;
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(outs[i], pk, workspace, need)) return MOSS_EALIAS;
+  if (overlaps(workspace, need, a, in) || overlaps(workspace, need, w_qkv, wb) ||
+      overlaps(workspace, need, rope, 8ull * rows * 64))
+    return MOSS_EALIAS;
+  const int rc = single_device_check();
+  if (rc != MOSS_OK) return rc;
+  float* rope_pp = static_cast<float*>(workspace);
+  MOSS_TRY(launch_rope_pairs(rope, rows, rope_pp, stream), "rope pairs");
+  MOSS_TRY(launch_gemm_qkv_pack(batch, rows, n_heads, eps, a, w_qkv, q_gain, k_gain, rope_pp, q, k, v, stream),
+           "gemm qkv + pack");
+  MOSS_TRY(launch_zero_packed_pads(batch, rows, n_heads, q, k, v, stream), "zero packed pads");
   return MOSS_OK;
 }
 

@@ -2,12 +2,13 @@
 // q/k gain, then the rotary rotation of interleaved pairs; v copied.  The
 // results are written in the packed layouts the attention kernel reads
 // (see moss.h): Q and K row-major per (item, head), V transposed per 64-key
-// tile with the keys of each 16-key group in the order 0-3, 8-11, 4-7, 12-15,
-// so that one 16-byte LDS read gives a lane the eight keys its MFMA operand
-// needs.
+// tile (dim-major, keys in order), so that a 16-byte read of a V^T row gives
+// eight consecutive keys of one dim.
 //
 // The MOSS-Image transformer page (TensorFold PR #1528, "What it adds") names
 // this kernel "q/k norm and rotary into packed rows".
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -16,13 +17,6 @@ namespace {
 constexpr int kTok = 64;      // tokens per workgroup
 constexpr int kThreads = 256; // 16 groups of 16 lanes; a group owns one 128-dim row
 constexpr int kVPitch = 136;  // LDS row pitch (bf16) of the V staging tile
-
-__device__ __forceinline__ int vperm(int p) {
-  // position within a 16-key group -> key (an involution: swap the middle quads)
-  const int q = (p >> 2) & 3;
-  const int qq = (q == 1) ? 2 : (q == 2 ? 1 : q);
-  return (p & ~15) | (qq << 2) | (p & 3);
-}
 
 __global__ __launch_bounds__(kThreads) void qk_norm_rope_pack_kernel(
     const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ q_gain, const uint16_t* __restrict__ k_gain,
@@ -92,20 +86,61 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_pack_kernel(
   uint16_t* vt = vo + (bh * (rows_pad / kTok) + tile) * (kTok * 128);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int id = tid + kThreads * i;  // 1024 chunks: dim = id / 8, positions 8*(id % 8) .. +7
+    const int id = tid + kThreads * i;  // 1024 chunks: dim = id / 8, keys t0 + 8*(id % 8) .. +7
     const int dim = id >> 3, pc = id & 7;
     uint32_t w[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int k0 = vperm(pc * 8 + 2 * e), k1 = vperm(pc * 8 + 2 * e + 1);
-      w[e] = (uint32_t)vs[k0 * kVPitch + dim] | ((uint32_t)vs[k1 * kVPitch + dim] << 16);
-    }
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)vs[(pc * 8 + 2 * e) * kVPitch + dim] | ((uint32_t)vs[(pc * 8 + 2 * e + 1) * kVPitch + dim] << 16);
     u32x4 out = {w[0], w[1], w[2], w[3]};
     reinterpret_cast<u32x4*>(vt)[id] = out;
   }
 }
 
+// Pad rows of the packed layouts: Q and K rows T..T_pad-1 (contiguous per
+// (item, head)) and V^T keys T..T_pad-1 of every dim row of the last tiles.
+__global__ __launch_bounds__(256) void zero_packed_pads_kernel(uint16_t* __restrict__ q, uint16_t* __restrict__ k,
+                                                               uint16_t* __restrict__ v, int rows, int rows_pad,
+                                                               int n_bh) {
+  const int npad = rows_pad - rows;
+  const long long per = (long long)npad * 128, total = per * n_bh;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (long long)gridDim.x * blockDim.x) {
+    const long long bh = i / per, r = i - bh * per;
+    q[(bh * rows_pad + rows) * 128 + r] = 0;
+    k[(bh * rows_pad + rows) * 128 + r] = 0;
+    const long long dim = r / npad, key = rows + (r - dim * npad);
+    v[((bh * (rows_pad / 64) + key / 64) * 128 + dim) * 64 + (key & 63)] = 0;
+  }
+}
+
+// rope [2][rows][64] -> rope_pp[cs][pp][t][2] (pairs of pairs, row stride rows_pad); one thread per
+// (cs, pp, t) moves one float2
+__global__ __launch_bounds__(256) void rope_pairs_kernel(const float* __restrict__ rope, int rows, int rows_pad,
+                                                         float* __restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;  // (cs * 32 + pp) * rows + t
+  if (i >= 64 * rows) return;
+  const int t = i % rows, cp = i / rows, cs = cp >> 5, pp = cp & 31;
+  const float2 v = *reinterpret_cast<const float2*>(rope + ((size_t)cs * rows + t) * 64 + 2 * pp);
+  *reinterpret_cast<float2*>(out + ((size_t)cp * rows_pad + t) * 2) = v;
+}
+
 }  // namespace
+
+hipError_t launch_rope_pairs(const float* rope, int rows, float* rope_pp, hipStream_t st) {
+  hipLaunchKernelGGL(rope_pairs_kernel, dim3((64 * rows + 255) / 256), dim3(256), 0, st, rope, rows,
+                     packed_rows(rows), rope_pp);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_packed_pads(int batch, int rows, int n_heads, uint16_t* q, uint16_t* k, uint16_t* v,
+                                   hipStream_t st) {
+  const int rp = packed_rows(rows);
+  if (rp == rows) return hipSuccess;
+  const long long total = (long long)(rp - rows) * 128 * batch * n_heads;
+  const int blocks = (int)std::min<long long>((total + 255) / 256, 4096);
+  hipLaunchKernelGGL(zero_packed_pads_kernel, dim3(blocks), dim3(256), 0, st, q, k, v, rows, rp, batch * n_heads);
+  return hipGetLastError();
+}
 
 hipError_t launch_qk_norm_rope_pack(int batch, int rows, int n_heads, float eps, const uint16_t* qkv,
                                     const uint16_t* q_gain, const uint16_t* k_gain, const float* rope,

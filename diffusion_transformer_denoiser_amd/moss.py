@@ -76,6 +76,8 @@ _SIGS = {
     "moss_k_gemm_nt": (ctypes.c_int, [c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_i32, c_vp, c_i32, c_vp]),
     "moss_k_qk_norm_rope_pack": (ctypes.c_int, [c_i32, c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                                 c_vp, c_vp]),
+    "moss_k_gemm_qkv_pack": (ctypes.c_int, [c_i32, c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                            c_vp, c_vp, c_size, c_vp]),
     "moss_k_attention": (ctypes.c_int, [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moss_k_silu_mul": (ctypes.c_int, [c_i32, c_i32, c_vp, c_vp, c_vp]),
     "moss_k_gated_add": (ctypes.c_int, [c_i32, c_i32, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp]),
@@ -277,6 +279,14 @@ def moss_k_gemm_nt(m, n, k, a, lda, w, ldw, c, ldc, stream=None) -> None:
 def moss_k_qk_norm_rope_pack(batch, rows, n_heads, eps, qkv, q_gain, k_gain, rope, q, k, v, stream=None) -> None:
     _check(lib().moss_k_qk_norm_rope_pack(batch, rows, n_heads, eps, _p(qkv), _p(q_gain), _p(k_gain), _p(rope),
                                           _p(q), _p(k), _p(v), _s(stream)), "moss_k_qk_norm_rope_pack")
+
+
+def moss_k_gemm_qkv_pack(batch, rows, n_heads, eps, a, w_qkv, q_gain, k_gain, rope, q, k, v, workspace,
+                         stream=None) -> None:
+    _check(lib().moss_k_gemm_qkv_pack(batch, rows, n_heads, eps, _p(a), _p(w_qkv), _p(q_gain), _p(k_gain), _p(rope),
+                                      _p(q), _p(k), _p(v), _p(workspace),
+                                      workspace.numel() * workspace.element_size(), _s(stream)),
+           "moss_k_gemm_qkv_pack")
 
 
 def moss_k_attention(batch, n_heads, rows, n_txt, txt_len, q, k, v, o, stream=None) -> None:

@@ -213,12 +213,12 @@ int moss_denoiser_forward(const moss_dims* dims, int32_t n_blocks, const uint16_
 
 /* ---- single-step entry points (same conventions; used by the tests) ----- */
 
-/* Packed attention layouts written by moss_k_qk_norm_rope_pack and read by
+/* Packed attention layouts written by moss_k_qk_norm_rope_pack and
+ * moss_k_gemm_qkv_pack and read by
  * moss_k_attention, with T_pad = moss_packed_rows(T) (T rounded up to 128):
  *   Q, K: [B, H, T_pad, 128] bf16; rows T..T_pad-1 are zero.
  *   V:    [B, H, T_pad/64, 128, 64] bf16: per 64-key tile, V transposed
- *         (dim-major) with the keys of each 16-key group stored in the order
- *         0-3, 8-11, 4-7, 12-15; keys T..T_pad-1 are zero. */
+ *         (dim-major) with the keys in order; keys T..T_pad-1 are zero. */
 int32_t moss_packed_rows(int32_t rows);
 
 /* a0: out[b, r] = r < n_txt ? (r < txt_len[b] ? txt[b, r] : 0) : x[b, r - n_txt];
@@ -248,6 +248,22 @@ int moss_k_mod_rmsnorm(int32_t batch, int32_t rows, int32_t d_model, float eps, 
  * adds"). */
 int moss_k_gemm_nt(int32_t m, int32_t n, int32_t k, const uint16_t* a, int32_t lda, const uint16_t* w,
                    int32_t ldw, uint16_t* c, int32_t ldc, hipStream_t stream);
+
+/* a3 + a4 as the block runs them: the QKV projection of a [B*T, D] (bf16,
+ * row stride D) by w_qkv [3D, D] with a4 applied to its fp32 sums after one
+ * bf16 rounding (the value the projection would store): q and k per row and
+ * head RMS-normed over the 128 dims, times q_gain / k_gain, rotated by rope;
+ * written packed as described above into q, k and v, pad rows zeroed.  D =
+ * 128 n_heads.  The bf16 GEMM and the "q/k norm and rotary into packed rows"
+ * kernel of the MOSS-Image transformer page ("What it adds"), fused so the
+ * qkv rows never reach memory.  Needs 512 * moss_packed_rows(rows) bytes of
+ * workspace (the rotary table re-laid for the epilogue's loads), else
+ * MOSS_EWORKSPACE; MOSS_EINVAL / MOSS_EALIAS as moss_k_qk_norm_rope_pack,
+ * the workspace included. */
+int moss_k_gemm_qkv_pack(int32_t batch, int32_t rows, int32_t n_heads, float eps, const uint16_t* a,
+                         const uint16_t* w_qkv, const uint16_t* q_gain, const uint16_t* k_gain, const float* rope,
+                         uint16_t* q, uint16_t* k, uint16_t* v, void* workspace, size_t ws_bytes,
+                         hipStream_t stream);
 
 /* a4: from qkv [B, T, 3D] (bf16), per row and head: q_hat = rotary(RMSNorm(q) * q_gain),
  * k_hat likewise with k_gain, v unchanged; written packed as described above
@@ -307,6 +323,8 @@ int moss_k_gated_add(int32_t batch, int32_t rows, int32_t d_model, float* h, con
  * moss_stack_forward, in order).  The gated adds and the SiLU gate run in the
  * epilogues of the out, down and up projections: MOSS_STEP_OUT, _UP and _DOWN
  * time the fused launches, and MOSS_STEP_GATE1, _SILU and _GATE2 record
+ * nothing.  The q/k norm, rotary and packing run in the QKV projection's
+ * epilogue: MOSS_STEP_QKV times the fused launch and MOSS_STEP_QKNORM records
  * nothing.  The row join runs in one pass with the first block's first norm:
  * MOSS_STEP_JOIN times that pass, and MOSS_STEP_NORM1 the first norms of the
  * later blocks of a stack. */

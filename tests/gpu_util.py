@@ -60,14 +60,6 @@ def sync():
 
 # ---- packed attention layouts (as documented in include/moss.h) ----------------
 
-def _vperm():
-    """Stored position -> key inside a 16-key group (0-3, 8-11, 4-7, 12-15)."""
-    p = np.arange(16)
-    q = p >> 2
-    qq = np.where(q == 1, 2, np.where(q == 2, 1, q))
-    return (qq << 2) | (p & 3)
-
-
 def pack_qk(x_bits: np.ndarray, rows_pad: int) -> np.ndarray:
     """[B, H, T, 128] bits -> [B, H, T_pad, 128] with zero pad rows."""
     b, h, t, d = x_bits.shape
@@ -77,24 +69,18 @@ def pack_qk(x_bits: np.ndarray, rows_pad: int) -> np.ndarray:
 
 
 def pack_v(v_bits: np.ndarray, rows_pad: int) -> np.ndarray:
-    """[B, H, T, 128] bits -> [B, H, T_pad/64, 128, 64] (transposed, keys permuted per 16)."""
+    """[B, H, T, 128] bits -> [B, H, T_pad/64, 128, 64] (per 64-key tile, transposed; zero pad keys)."""
     b, h, t, d = v_bits.shape
     full = np.zeros((b, h, rows_pad, d), dtype=np.uint16)
     full[:, :, :t] = v_bits
     tiles = full.reshape(b, h, rows_pad // 64, 64, d)  # [.., tile, key, dim]
-    perm = (np.arange(64) & ~15) | _vperm()[np.arange(64) & 15]  # position -> key
-    tiles = tiles[:, :, :, perm, :]
     return np.ascontiguousarray(tiles.transpose(0, 1, 2, 4, 3))
 
 
 def unpack_v(packed_bits: np.ndarray, rows: int) -> np.ndarray:
     """Inverse of pack_v: -> [B, H, T, 128] bits (and the pad keys separately)."""
     b, h, nt, d, _ = packed_bits.shape
-    tiles = packed_bits.transpose(0, 1, 2, 4, 3)  # [.., tile, position, dim]
-    perm = (np.arange(64) & ~15) | _vperm()[np.arange(64) & 15]
-    keys = np.empty_like(tiles)
-    keys[:, :, :, perm, :] = tiles
-    full = keys.reshape(b, h, nt * 64, d)
+    full = packed_bits.transpose(0, 1, 2, 4, 3).reshape(b, h, nt * 64, d)
     return full[:, :, :rows], full[:, :, rows:]
 
 

@@ -63,8 +63,8 @@ def test_status_strings():
 def test_workspace_bytes():
     d = c2_dims()
     ws = moss.moss_workspace_bytes(d, 1)
-    # fp32 residual (50.7 MB) + a (25.4 MB) + the union of {qkv 76.1 MB + packed q/k/v 77.9 MB} and z (101.5 MB)
-    assert 225 * MB < ws < 235 * MB, ws
+    # fp32 residual (50.7 MB) + a (25.4 MB) + packed q/k/v (3 x 26.0 MB) + z (101.5 MB)
+    assert 250 * MB < ws < 260 * MB, ws
     assert moss.moss_workspace_bytes(d, 24) == ws
     assert moss.moss_workspace_bytes(c2_dims(batch=2), 1) > ws
     assert moss.moss_workspace_bytes(c2_dims(head_dim=64), 1) == 0
@@ -158,6 +158,12 @@ def test_single_step_entry_points_validate():
     assert L.moss_k_qk_norm_rope_pack(1, 10, 2, 1e-6, fake(1), fake(2), fake(3), fake(4), fake(5), fake(5), fake(6),
                                       None) == moss.MOSS_EALIAS
     assert L.moss_k_adaln_gemv(1, 256, fake(1), fake(2), fake(3), fake(4), 100, None) == moss.MOSS_EWORKSPACE
+    # the fused QKV step: 10 rows pack to 128, so it needs 512 * 128 bytes of workspace
+    qkv_args = (1, 10, 2, 1e-6, fake(1), fake(2), fake(3), fake(4), fake(5), fake(6), fake(7), fake(8))
+    assert L.moss_k_gemm_qkv_pack(*qkv_args, fake(9), 512 * 128 - 1, None) == moss.MOSS_EWORKSPACE
+    assert L.moss_k_gemm_qkv_pack(*qkv_args, None, 512 * 128, None) == moss.MOSS_EWORKSPACE
+    assert L.moss_k_gemm_qkv_pack(*qkv_args, fake(6), 512 * 128, None) == moss.MOSS_EALIAS  # workspace on q
+    assert L.moss_k_gemm_qkv_pack(1, 10, 2, 0.0, *qkv_args[4:], fake(9), 512 * 128, None) == moss.MOSS_EINVAL
     assert L.moss_rope_build(-1, 4, 4, 10000.0, fake(1), None) == moss.MOSS_EINVAL
     assert L.moss_rope_build(2, 4, 4, 1.0, fake(1), None) == moss.MOSS_EINVAL
 

@@ -236,6 +236,54 @@ def test_qk_norm_rope_pack(batch, n_txt, gh, gw, heads):
     assert np.all(qb[:, :, rows:] == 0) and np.all(kb[:, :, rows:] == 0) and np.all(vpad == 0)
 
 
+@pytest.mark.parametrize("batch,n_txt,gh,gw,heads", [
+    (1, 8, 8, 8, 2),      # one 128-row tile of rows, two heads
+    (2, 34, 8, 12, 3),    # items that straddle row tiles; D = 384: a tile spans q and k columns
+    (1, 34, 64, 64, 24),  # the 4096+34-row QKV (column split: the last 6 column tiles run as 128-row tiles)
+])
+def test_gemm_qkv_pack(batch, n_txt, gh, gw, heads):
+    """a3 + a4 fused: the QKV projection with the q/k norm, rotary and packing in its epilogue, against
+    the oracle's a4 on the bf16-rounded projection (the value the unfused path stores)."""
+    rows = n_txt + gh * gw
+    d = heads * 128
+    G.say(f"gemm_qkv_pack B={batch} rows={rows} H={heads}")
+    a = synth.make_tensor(10, 0, (batch * rows, d))
+    w = synth.make_tensor(10, 1, (3 * d, d), std=0.02)
+    gq = synth.normal_bf16(10, (0, 50), (128,), 0.02, offset=1.0)
+    gk = synth.normal_bf16(10, (0, 51), (128,), 0.02, offset=1.0)
+    rope = G.empty_f32(2, rows, 64)
+    moss.moss_rope_build(n_txt, gh, gw, 10000.0, rope)
+    rp = moss.moss_packed_rows(rows)
+    q = G.empty_bf16(batch, heads, rp, 128)
+    k = G.empty_bf16(batch, heads, rp, 128)
+    v = G.empty_bf16(batch, heads, rp // 64, 128, 64)
+    for t_ in (q, k, v):
+        t_.fill_(0x7FC0)  # NaN pattern: every element must be written
+    ws = G.empty_f32(128 * rp)  # the rotary table re-laid for the epilogue: 512 T_pad bytes
+    moss.moss_k_gemm_qkv_pack(batch, rows, heads, 1e-6, G.dev(a), G.dev(w), G.dev(gq), G.dev(gk), rope, q, k, v, ws)
+    G.sync()
+    cos, sin = ob.rope_tables(n_txt, gh, gw, 10000.0, 128)
+    # sampled rows at the full size, all rows otherwise
+    sel = np.arange(rows) if rows <= 1100 else np.unique(np.r_[0:40, rows - 40:rows,
+                                                                 np.linspace(0, rows - 1, 120).astype(int)])
+    qb, kb = G.host_bits(q), G.host_bits(k)
+    vb, vpad = G.unpack_v(G.host_bits(v), rows)
+    for b in range(batch):
+        arows = ob.widen_bf16(a.reshape(batch, rows, d)[b][sel])
+        qkv = ob.round_bf16(arows @ ob.widen_bf16(w).T).reshape(len(sel), 3, heads, 128).transpose(1, 2, 0, 3)
+        rq, rk = ob.qk_norm_rope(qkv[0], qkv[1], ob.widen_bf16(gq), ob.widen_bf16(gk), cos[sel], sin[sel], 1e-6)
+        # The projection's fp32 sum can round to the other bf16 neighbour of the exact sum (as the
+        # unfused GEMM's output can); such an input flip moves a normed value by about 2^-8 of the
+        # row scale (about 1), hence the 8e-3 floor; nearly all values must agree to one ulp.
+        for name, got, ref in ((f"q[{b}]", ob.widen_bf16(qb[b][:, sel]), rq),
+                               (f"k[{b}]", ob.widen_bf16(kb[b][:, sel]), rk)):
+            G.assert_ulps(name, got, ref, ulps=2.0, abs_floor=8e-3)
+            tight = np.abs(got - ref) <= G.bf16_ulp(ref) + 2e-5
+            assert tight.mean() >= 0.999, f"{name}: {100 * (1 - tight.mean()):.3f}% beyond one ulp"
+        G.assert_ulps(f"v[{b}]", ob.widen_bf16(vb[b][:, sel]), qkv[2], ulps=1.0, abs_floor=2e-6 * np.sqrt(d))
+    assert np.all(qb[:, :, rows:] == 0) and np.all(kb[:, :, rows:] == 0) and np.all(vpad == 0)
+
+
 # ---- a5 attention -------------------------------------------------------------------------------------
 
 def _attention_case(batch, heads, rows, n_txt, lens, seed, q_scale=1.0, qkv_bits=None):
