@@ -294,13 +294,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const uint16_t* _
     pv(t - 1);
     qk(t);
 #if MOSS_ATTN_SCHED
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, MOSS_ATTN_SCHED, 0);
 #pragma unroll
-    for (int q = 0; q < 28; ++q) {
+    for (int q = 0; q < 32 - MOSS_ATTN_SCHED; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MOSS_ATTN_SCHED, 0);
 #endif
   };
   // Both groups pass the same n_tiles + 1 workgroup barriers (the first one above).

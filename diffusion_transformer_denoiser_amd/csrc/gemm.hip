@@ -193,14 +193,12 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[BN / WN / 32][BM / 
 // kQkvPack: the QKV projection with a4 in its epilogue.  Each value is first
 // rounded to bf16, as the projection output would store it.  A wavefront owns
 // 64 columns, half of one head of q, k or v; for q and k the per-(row, head)
-// sum of squares adds the partner wavefront's half through LDS, then each
-// value is scaled by 1/sqrt(mean + eps) and the gain and its pair rotated,
+// sum of squares (of the fp32 sums) adds the partner wavefront's half through
+// LDS, then each value is scaled by 1/sqrt(mean + eps) and the gain and its
+// pair rotated,
 // and the row goes to the packed Q or K layout [B, H, T_pad, 128].  v values
 // go to V^T [B, H, T_pad/64, 128, 64] one bf16 at a time (the 32 lanes of a
 // half wavefront write 32 consecutive keys of one dim: one 64-byte segment).
-#ifndef MOSS_QKV_SS_ROUNDED
-#define MOSS_QKV_SS_ROUNDED 1
-#endif
 template <int BM, int BN, int WM, int WN>
 __device__ __forceinline__ void epilogue_qkv(const f32x16 (&acc)[BN / WN / 32][BM / WM / 32], char* smem, int m0,
                                              int n0, int wave, int wm, int wn, int l32, int hh, int m,
@@ -212,14 +210,10 @@ __device__ __forceinline__ void epilogue_qkv(const f32x16 (&acc)[BN / WN / 32][B
   const int col = ep.col0 + n0 + wn * TN;  // this wavefront's first column of [q | k | v]
   const int which = col / D, head = (col - which * D) >> 7, half = ((col - which * D) >> 6) & 1;
 
-  // the value as the projection output would store it, rounded where used rather than kept (the
-  // sums of squares round with integer arithmetic, to the same nearest-even bf16 for finite values,
-  // so the compiler does not keep those results live across the barrier for the second use)
+  // the value as the projection output would store it (rounded where used, not kept in registers)
   auto xr = [&](int i, int j, int e) { return (float)(__bf16)acc[i][j][e]; };
-  auto xr_int = [&](int i, int j, int e) {
-    const uint32_t u = __float_as_uint(acc[i][j][e]);
-    return __uint_as_float((u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u);
-  };
+  // per-row sums of squares over the fp32 sums (before the bf16 rounding; the scale differs from
+  // the rounded values' by about 1e-5 relative, far inside a bf16 ulp, and costs no rounding here)
   float ss[FM];
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
@@ -227,14 +221,7 @@ __device__ __forceinline__ void epilogue_qkv(const f32x16 (&acc)[BN / WN / 32][B
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-#if MOSS_QKV_SS_ROUNDED
-        const float v = xr_int(i, j, e);
-#else
-        const float v = acc[i][j][e];
-#endif
-        sj += v * v;
-      }
+      for (int e = 0; e < 16; ++e) sj += acc[i][j][e] * acc[i][j][e];
     ss[j] = sj + __shfl_xor(sj, 32, 64);  // the wavefront's 64 columns of row j*32 + l32
   }
   float* ss_lds = reinterpret_cast<float*>(smem);  // [wavefront][TM]; the K loop's last reads are done

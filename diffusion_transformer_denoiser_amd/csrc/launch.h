@@ -55,6 +55,10 @@ hipError_t launch_rope_pairs(const float* rope, int rows, float* rope_pp, hipStr
 hipError_t launch_gemm_qkv_pack(int batch, int rows, int n_heads, float eps, const uint16_t* a, const uint16_t* w_qkv,
                                 const uint16_t* q_gain, const uint16_t* k_gain, const float* rope_pp, uint16_t* q,
                                 uint16_t* k, uint16_t* v, hipStream_t st);
+// Once per call, one launch: s = SiLU(cond) (n_cond values), rope_pp as launch_rope_pairs, and
+// the pad rows zeroed as launch_zero_packed_pads.
+hipError_t launch_call_prologue(const uint16_t* cond, float* s, int n_cond, const float* rope, int batch, int rows,
+                                int n_heads, float* rope_pp, uint16_t* q, uint16_t* k, uint16_t* v, hipStream_t st);
 // Zero the pad rows T..T_pad-1 of packed Q and K and the pad keys of V^T.
 hipError_t launch_zero_packed_pads(int batch, int rows, int n_heads, uint16_t* q, uint16_t* k, uint16_t* v,
                                    hipStream_t st);

@@ -287,15 +287,14 @@ int run_stack(const Ctx& c, int n_blocks, const uint16_t* x, const uint16_t* txt
               const moss_block_weights* blocks, const float* rope, uint16_t* out, const uint8_t* skip) {
   const moss_dims* d = c.d;
   float* h = reinterpret_cast<float*>(c.ws + c.L.h);
-  MOSS_TRY(launch_silu_cond(cond, reinterpret_cast<float*>(c.ws + c.L.s_cond), d->batch, d->d_model, c.st),
-           "silu_cond");
-  MOSS_TRY(launch_zero_packed_pads(d->batch, d->n_txt + d->n_img, d->n_heads,
-                                   reinterpret_cast<uint16_t*>(c.ws + c.L.qp),
-                                   reinterpret_cast<uint16_t*>(c.ws + c.L.kp),
-                                   reinterpret_cast<uint16_t*>(c.ws + c.L.vp), c.st),
-           "zero packed pads");
-  MOSS_TRY(launch_rope_pairs(rope, d->n_txt + d->n_img, reinterpret_cast<float*>(c.ws + c.L.rope_pp), c.st),
-           "rope pairs");
+  // SiLU(cond), the re-laid rotary table and the packed pad rows, once per call
+  MOSS_TRY(launch_call_prologue(cond, reinterpret_cast<float*>(c.ws + c.L.s_cond), d->batch * d->d_model, rope,
+                                d->batch, d->n_txt + d->n_img, d->n_heads,
+                                reinterpret_cast<float*>(c.ws + c.L.rope_pp),
+                                reinterpret_cast<uint16_t*>(c.ws + c.L.qp),
+                                reinterpret_cast<uint16_t*>(c.ws + c.L.kp),
+                                reinterpret_cast<uint16_t*>(c.ws + c.L.vp), c.st),
+           "call prologue");
   for (int i = 0; i < n_blocks; ++i) {
     unsigned mask = 0;
     if (skip)

@@ -124,7 +124,47 @@ __global__ __launch_bounds__(256) void rope_pairs_kernel(const float* __restrict
   *reinterpret_cast<float2*>(out + ((size_t)cp * rows_pad + t) * 2) = v;
 }
 
+// The once-per-call preparation of a block stack in one launch: SiLU(cond)
+// for the modulation GEMVs, the rotary table as pairs of pairs for the QKV
+// epilogue, and zeros in the pad rows of packed Q, K and V^T.  One flat
+// index runs over the three jobs in turn.
+__global__ __launch_bounds__(256) void call_prologue_kernel(const uint16_t* __restrict__ cond, float* __restrict__ s,
+                                                            int n_cond, const float* __restrict__ rope, int rows,
+                                                            int rows_pad, float* __restrict__ rope_pp,
+                                                            uint16_t* __restrict__ q, uint16_t* __restrict__ k,
+                                                            uint16_t* __restrict__ v, int n_bh) {
+  const long long n1 = n_cond, n2 = 64LL * rows, npad = rows_pad - rows, n3 = npad * 128 * n_bh;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n1 + n2 + n3;
+       i += (long long)gridDim.x * blockDim.x) {
+    if (i < n1) {
+      s[i] = silu_f32(bf16_to_f32(cond[i]));
+    } else if (i < n1 + n2) {
+      const long long j = i - n1;  // (cs * 32 + pp) * rows + t
+      const long long t = j % rows, cp = j / rows, cs = cp >> 5, pp = cp & 31;
+      const float2 val = *reinterpret_cast<const float2*>(rope + (cs * rows + t) * 64 + 2 * pp);
+      *reinterpret_cast<float2*>(rope_pp + (cp * rows_pad + t) * 2) = val;
+    } else {
+      const long long j = i - n1 - n2, per = npad * 128;
+      const long long bh = j / per, r = j - bh * per;
+      q[(bh * rows_pad + rows) * 128 + r] = 0;
+      k[(bh * rows_pad + rows) * 128 + r] = 0;
+      const long long dim = r / npad, key = rows + (r - dim * npad);
+      v[((bh * (rows_pad / 64) + key / 64) * 128 + dim) * 64 + (key & 63)] = 0;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_call_prologue(const uint16_t* cond, float* s, int n_cond, const float* rope, int batch, int rows,
+                                int n_heads, float* rope_pp, uint16_t* q, uint16_t* k, uint16_t* v, hipStream_t st) {
+  const int rp = packed_rows(rows);
+  const long long total = (long long)n_cond + 64LL * rows + (long long)(rp - rows) * 128 * batch * n_heads;
+  const int blocks = (int)std::min<long long>((total + 255) / 256, 2048);
+  hipLaunchKernelGGL(call_prologue_kernel, dim3(blocks), dim3(256), 0, st, cond, s, n_cond, rope, rows, rp, rope_pp,
+                     q, k, v, batch * n_heads);
+  return hipGetLastError();
+}
 
 hipError_t launch_rope_pairs(const float* rope, int rows, float* rope_pp, hipStream_t st) {
   hipLaunchKernelGGL(rope_pairs_kernel, dim3((64 * rows + 255) / 256), dim3(256), 0, st, rope, rows,
