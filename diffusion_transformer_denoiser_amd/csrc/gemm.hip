@@ -2,9 +2,10 @@
 // sums and a bf16 result (the MOSS-Image transformer page, TensorFold PR #1528,
 // "What it adds": bf16 GEMMs with fp32 sums).
 //
-// gfx950 design.  A workgroup of 8 wavefronts computes a 256 x BN tile of c
-// with v_mfma_f32_32x32x16_bf16; each wavefront owns a (256/WM) x (BN/WN)
-// sub-tile whose fp32 accumulators stay in registers for the whole K loop.
+// gfx950 design.  A workgroup of 8 wavefronts computes a BM x BN tile of c
+// (256 x 256 mostly) with v_mfma_f32_32x32x16_bf16; each wavefront owns a
+// (BM/WM) x (BN/WN) sub-tile whose fp32 accumulators stay in registers for
+// the whole K loop.
 //
 //  * K advances 32 at a time through a ring of LDS stages (five, 160 KiB, for
 //    the 256 x 256 tiles).  Each slab is fetched straight into LDS with
@@ -118,11 +119,13 @@ __device__ __forceinline__ void wait_slabs_barrier(int ahead) {
 // still has several MFMAs behind it before its data are needed.
 template <int RPM, int NR, int NMFMA>
 __device__ __forceinline__ void sched_interleave() {
-  if constexpr (NR > 0) {
+  if constexpr (NR > 0 && NMFMA > 0) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, NR < RPM ? NR : RPM, 0);
     sched_interleave<RPM, (NR > RPM ? NR - RPM : 0), NMFMA - 1>();
-  } else {
+  } else if constexpr (NR > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+  } else if constexpr (NMFMA > 0) {
     __builtin_amdgcn_sched_group_barrier(0x008, NMFMA, 0);
   }
 }
@@ -306,9 +309,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
   constexpr int AB = BM * KB * 2, BB = BN * KB * 2;          // bytes per slab
-  constexpr int LA = AB / 1024 / NW, LB = BB / 1024 / NW;    // 1 KiB load instructions per wavefront
+  // 1 KiB load instructions per wavefront; when the A chunks do not divide among the wavefronts
+  // (224-row tiles: 14 chunks), the last wavefronts load the last chunk again (same bytes, same place)
+  constexpr int CA = AB / 1024, CB = BB / 1024;
+  constexpr int LA = (CA + NW - 1) / NW, LB = CB / NW;
   constexpr int PER = LA + LB;
-  static_assert(LA * NW * 1024 == AB && LB * NW * 1024 == BB, "slab / wavefront mismatch");
+  static_assert(CA * 1024 == AB && LB * NW * 1024 == BB, "slab / wavefront mismatch");
   static_assert(STAGES >= 4 && (STAGES - 3) * PER <= 63, "ring depth / vmcnt range");
   static_assert(EPI != kSiluGate || FN % 2 == 0, "the SiLU epilogue pairs gate and up fragments per wavefront");
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * (AB + BB)];
@@ -325,9 +331,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
   // Rows past m are clamped to m - 1; their results are never stored.
   const uint16_t* ga[LA];
   const uint16_t* gb[LB];
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t ca[LA];  // LDS byte offset of A chunk i of this wavefront
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
-    const int r = (wave + NW * i) * 16 + (lane >> 2);
+    const int chunk = min(wv + NW * i, CA - 1);
+    ca[i] = 1024u * chunk;
+    const int r = chunk * 16 + (lane >> 2);
     ga[i] = a + (size_t)min(m0 + r, m - 1) * lda + ((lane & 3) ^ ((r >> 2) & 3)) * 8;
   }
 #pragma unroll
@@ -343,13 +353,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
     }
     gb[i] = w + (size_t)wrow * ldw + ((lane & 3) ^ ((r >> 2) & 3)) * 8;
   }
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(MOSS_LDS char*)smem + 1024u * __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(MOSS_LDS char*)smem;
   auto issue = [&](int slab) {
     const uint32_t base = lds0 + (uint32_t)((slab % STAGES) * (AB + BB));
 #pragma unroll
-    for (int i = 0; i < LA; ++i) dma16(ga[i] + slab * KB, base + 1024u * NW * i);
+    for (int i = 0; i < LA; ++i) dma16(ga[i] + slab * KB, base + ca[i]);
 #pragma unroll
-    for (int i = 0; i < LB; ++i) dma16(gb[i] + slab * KB, base + AB + 1024u * NW * i);
+    for (int i = 0; i < LB; ++i) dma16(gb[i] + slab * KB, base + AB + 1024u * (wv + NW * i));
   };
   // byte offsets of this lane's fragments within a stage, for the two k16 steps of a slab
   int offa[2][FM], offb[2][FN];
@@ -474,6 +484,19 @@ hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_
       }
     }
     const int m_main = split ? full * 256 : m;
+    if constexpr (EPI == kGatedAdd) {
+      // 224-row tiles when they take no more rounds over the CUs than 256-row ones: each CU then
+      // does 7/8 of the work (the out and down projections' one part-full round at 4096+34 rows:
+      // 204 tiles of 256 rows or 228 of 224 on 256 CUs).  Eight wavefronts of 224 x 32 (8 fragment
+      // reads per 7 MFMAs against 6 per 8) keep most of the saving: down 331 -> 318 us; four of
+      // 224 x 64 (1 per SIMD) kept less.
+      const int t256 = ((m + 255) / 256) * nt, t224 = ((m + 223) / 224) * nt;
+      if (!split && (t224 + cus - 1) / cus == (t256 + cus - 1) / cus) {
+        hipLaunchKernelGGL((gemm_nt_kernel<224, 256, 1, 8, EPI, 5>), dim3(t224), dim3(512), 0, st, a, lda, w, ldw, c,
+                           ldc, 0, m, n, k, ep);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI, 5>), dim3(((m_main + 255) / 256) * nt), dim3(512), 0, st,
                        a, lda, w, ldw, c, ldc, 0, m_main, n, k, ep);
     if (split) {
