@@ -96,72 +96,89 @@ __global__ __launch_bounds__(kThreads) void adaln_gemv_kernel(const float* __res
   }
 }
 
-// The second half of a modulated RMSNorm row held by one wavefront (CPL chunks
-// of eight values per lane, ss = this lane's sum of squares): the shift and
-// scale loads go out before the cross-lane reduction they do not depend on.
-template <int CPL>
-__device__ __forceinline__ void modulate_store(const f32x4 (&v)[CPL][2], float ss, const float* __restrict__ sh,
-                                               const float* __restrict__ sc, u32x4* __restrict__ dst, int lane,
-                                               int nch, int d, float eps) {
-  f32x4 shv[CPL][2], scv[CPL][2];
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nch) {
-      shv[i][0] = reinterpret_cast<const f32x4*>(sh + 8 * c)[0];
-      shv[i][1] = reinterpret_cast<const f32x4*>(sh + 8 * c)[1];
-      scv[i][0] = reinterpret_cast<const f32x4*>(sc + 8 * c)[0];
-      scv[i][1] = reinterpret_cast<const f32x4*>(sc + 8 * c)[1];
-    }
-  }
+// Row layout for the norms below: lane l's chunk i holds values 4 (l + 64 i) .. +3, so each
+// load or store instruction of a wavefront covers one contiguous stretch of the row (1 KiB of
+// fp32, 512 B of bf16).  The shift and scale of a chunk are loaded where they are used, which
+// keeps the register count (and so the wavefronts in flight per SIMD) up.
+template <int C4>
+__device__ __forceinline__ void modulate_store(const f32x4 (&v)[C4], float ss, const float* __restrict__ sh,
+                                                const float* __restrict__ sc, uint16_t* __restrict__ dst, int lane,
+                                                int nch4, int d, float eps) {
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)d + eps);
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) {
+  for (int i = 0; i < C4; ++i) {
     const int c = lane + 64 * i;
-    if (c < nch) {
-      float o[8];
+    if (c < nch4) {
+      const f32x4 shv = reinterpret_cast<const f32x4*>(sh)[c];
+      const f32x4 scv = reinterpret_cast<const f32x4*>(sc)[c];
+      float o[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        o[j] = (v[i][0][j] * r) * (1.0f + scv[i][0][j]) + shv[i][0][j];
-        o[4 + j] = (v[i][1][j] * r) * (1.0f + scv[i][1][j]) + shv[i][1][j];
-      }
-      dst[c] = pack8(o);
+      for (int j = 0; j < 4; ++j) o[j] = (v[i][j] * r) * (1.0f + scv[j]) + shv[j];
+      reinterpret_cast<u32x2*>(dst)[c] = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
     }
   }
 }
 
-// ---- a2/a8: modulated RMSNorm of the fp32 residual, one wavefront per row ----
-// The row stays in registers between the mean-square pass and the scaling
-// pass: CPL chunks of eight values per lane (CPL * 512 >= d_model).
-template <int CPL>
+template <int C4>
 __global__ __launch_bounds__(kThreads) void mod_rmsnorm_kernel(const float* __restrict__ h,
-                                                               const float* __restrict__ shift,
-                                                               const float* __restrict__ scale,
-                                                               int mod_stride, uint16_t* __restrict__ out,
-                                                               int total_rows, int rows_per_item, int d,
-                                                               float eps) {
+                                                                const float* __restrict__ shift,
+                                                                const float* __restrict__ scale, int mod_stride,
+                                                                uint16_t* __restrict__ out, int total_rows,
+                                                                int rows_per_item, int d, float eps) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (row >= total_rows) return;
   const int b = row / rows_per_item;
-  const int nch = d >> 3;
+  const int nch4 = d >> 2;
   const f32x4* src = reinterpret_cast<const f32x4*>(h + (size_t)row * d);
-  f32x4 v[CPL][2];
+  f32x4 v[C4];
   float ss = 0.0f;
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) {
+  for (int i = 0; i < C4; ++i) {
     const int c = lane + 64 * i;
-    if (c < nch) {
-      v[i][0] = src[2 * c];
-      v[i][1] = src[2 * c + 1];
+    if (c < nch4) {
+      v[i] = src[c];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ss += v[i][0][j] * v[i][0][j] + v[i][1][j] * v[i][1][j];
+      for (int j = 0; j < 4; ++j) ss += v[i][j] * v[i][j];
     }
   }
-  modulate_store<CPL>(v, ss, shift + (size_t)b * mod_stride, scale + (size_t)b * mod_stride,
-                      reinterpret_cast<u32x4*>(out + (size_t)row * d), lane, nch, d, eps);
+  modulate_store<C4>(v, ss, shift + (size_t)b * mod_stride, scale + (size_t)b * mod_stride, out + (size_t)row * d,
+                      lane, nch4, d, eps);
 }
+
+template <int C4>
+__global__ __launch_bounds__(kThreads) void join_mod_rmsnorm_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ txt, ItemLens lens, const float* __restrict__ shift,
+    const float* __restrict__ scale, int mod_stride, float* __restrict__ h, uint16_t* __restrict__ out,
+    int n_txt, int n_img, int d, float eps, int total_rows) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= total_rows) return;
+  const int rows = n_txt + n_img;
+  const int b = row / rows, r = row - b * rows;
+  const int nch4 = d >> 2;
+  const u32x2* src = nullptr;
+  if (r >= n_txt) src = reinterpret_cast<const u32x2*>(x + ((size_t)b * n_img + (r - n_txt)) * d);
+  else if (r < lens.len[b]) src = reinterpret_cast<const u32x2*>(txt + ((size_t)b * n_txt + r) * d);
+  f32x4 v[C4];
+  float ss = 0.0f;
+  f32x4* hrow = reinterpret_cast<f32x4*>(h + (size_t)row * d);
+#pragma unroll
+  for (int i = 0; i < C4; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch4) {
+      const u32x2 w = src ? src[c] : u32x2{0u, 0u};
+      v[i] = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+      hrow[c] = v[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ss += v[i][j] * v[i][j];
+    }
+  }
+  modulate_store<C4>(v, ss, shift + (size_t)b * mod_stride, scale + (size_t)b * mod_stride, out + (size_t)row * d,
+                      lane, nch4, d, eps);
+}
+
 
 // ---- a7/a12: h + gate * y on the fp32 residual ------------------------------------
 // In place (out16 == nullptr), or, for the last add of a call, into the bf16
@@ -198,40 +215,6 @@ __global__ __launch_bounds__(kThreads) void gated_add_kernel(f32x4* __restrict__
 // ---- a0 + a2 for a call's first block: join the rows into the fp32 residual
 // and apply the first modulated RMSNorm, one wavefront per row, so h is
 // written once and not read back.  Text pad rows (r >= txt_len) are zero rows.
-template <int CPL>
-__global__ __launch_bounds__(kThreads) void join_mod_rmsnorm_kernel(
-    const u32x4* __restrict__ x, const u32x4* __restrict__ txt, ItemLens lens, const float* __restrict__ shift,
-    const float* __restrict__ scale, int mod_stride, float* __restrict__ h, uint16_t* __restrict__ out,
-    int n_txt, int n_img, int d, float eps, int total_rows) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (row >= total_rows) return;
-  const int rows = n_txt + n_img;
-  const int b = row / rows, r = row - b * rows;
-  const int nch = d >> 3;
-  const u32x4* src = nullptr;
-  if (r >= n_txt) src = x + ((size_t)b * n_img + (r - n_txt)) * nch;
-  else if (r < lens.len[b]) src = txt + ((size_t)b * n_txt + r) * nch;
-  f32x4 v[CPL][2];
-  float ss = 0.0f;
-  f32x4* hrow = reinterpret_cast<f32x4*>(h + (size_t)row * d);
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nch) {
-      float f[8];
-      unpack8(src ? src[c] : u32x4{0u, 0u, 0u, 0u}, f);
-      v[i][0] = f32x4{f[0], f[1], f[2], f[3]};
-      v[i][1] = f32x4{f[4], f[5], f[6], f[7]};
-      hrow[2 * c] = v[i][0];
-      hrow[2 * c + 1] = v[i][1];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ss += f[j] * f[j];
-    }
-  }
-  modulate_store<CPL>(v, ss, shift + (size_t)b * mod_stride, scale + (size_t)b * mod_stride,
-                      reinterpret_cast<u32x4*>(out + (size_t)row * d), lane, nch, d, eps);
-}
 
 // ---- a10: z = SiLU(u_gate) * u_up -------------------------------------------
 __global__ __launch_bounds__(kThreads) void silu_mul_kernel(const uint16_t* __restrict__ u, u32x4* __restrict__ z,
@@ -368,20 +351,17 @@ hipError_t launch_adaln_gemv(const float* s, const uint16_t* w_mod, float* mod, 
 hipError_t launch_mod_rmsnorm(const float* h, const float* shift, const float* scale, int mod_stride,
                               uint16_t* out, int batch, int rows, int d, float eps, hipStream_t st) {
   const int total = batch * rows;
-  const int cpl = (d / 8 + 63) / 64;
+  const int c4 = (d / 4 + 63) / 64;
   const dim3 grid((total + 3) / 4), block(kThreads);
-  if (cpl <= 2)
-    hipLaunchKernelGGL(mod_rmsnorm_kernel<2>, grid, block, 0, st, h, shift, scale, mod_stride, out, total, rows, d, eps);
-  else if (cpl <= 4)
-    hipLaunchKernelGGL(mod_rmsnorm_kernel<4>, grid, block, 0, st, h, shift, scale, mod_stride, out, total, rows, d, eps);
-  else if (cpl <= 6)
-    hipLaunchKernelGGL(mod_rmsnorm_kernel<6>, grid, block, 0, st, h, shift, scale, mod_stride, out, total, rows, d, eps);
-  else if (cpl <= 8)
-    hipLaunchKernelGGL(mod_rmsnorm_kernel<8>, grid, block, 0, st, h, shift, scale, mod_stride, out, total, rows, d, eps);
-  else
-    hipLaunchKernelGGL(mod_rmsnorm_kernel<16>, grid, block, 0, st, h, shift, scale, mod_stride, out, total, rows, d,
-                       eps);
-  return hipGetLastError();
+#define MOSS_NORM_CASE(N)                                                                                        \
+  if (c4 <= N) {                                                                                                 \
+    hipLaunchKernelGGL(mod_rmsnorm_kernel<N>, grid, block, 0, st, h, shift, scale, mod_stride, out, total, rows, \
+                       d, eps);                                                                                  \
+    return hipGetLastError();                                                                                    \
+  }
+  MOSS_NORM_CASE(4) MOSS_NORM_CASE(8) MOSS_NORM_CASE(12) MOSS_NORM_CASE(16) MOSS_NORM_CASE(32)
+#undef MOSS_NORM_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gated_add(float* h, const float* gate, int gate_stride, const uint16_t* y, uint16_t* out16,
@@ -420,26 +400,17 @@ hipError_t launch_join_mod_rmsnorm(const uint16_t* x, const uint16_t* txt, const
                                    const float* scale, int mod_stride, float* h, uint16_t* out, int batch, int n_txt,
                                    int n_img, int d, float eps, hipStream_t st) {
   const int total = batch * (n_txt + n_img);
-  const int cpl = (d / 8 + 63) / 64;
+  const int c4 = (d / 4 + 63) / 64;
   const dim3 grid((total + 3) / 4), block(kThreads);
-  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
-  const u32x4* tv = reinterpret_cast<const u32x4*>(txt);
-  if (cpl <= 2)
-    hipLaunchKernelGGL(join_mod_rmsnorm_kernel<2>, grid, block, 0, st, xv, tv, lens, shift, scale, mod_stride, h, out,
-                       n_txt, n_img, d, eps, total);
-  else if (cpl <= 4)
-    hipLaunchKernelGGL(join_mod_rmsnorm_kernel<4>, grid, block, 0, st, xv, tv, lens, shift, scale, mod_stride, h, out,
-                       n_txt, n_img, d, eps, total);
-  else if (cpl <= 6)
-    hipLaunchKernelGGL(join_mod_rmsnorm_kernel<6>, grid, block, 0, st, xv, tv, lens, shift, scale, mod_stride, h, out,
-                       n_txt, n_img, d, eps, total);
-  else if (cpl <= 8)
-    hipLaunchKernelGGL(join_mod_rmsnorm_kernel<8>, grid, block, 0, st, xv, tv, lens, shift, scale, mod_stride, h, out,
-                       n_txt, n_img, d, eps, total);
-  else
-    hipLaunchKernelGGL(join_mod_rmsnorm_kernel<16>, grid, block, 0, st, xv, tv, lens, shift, scale, mod_stride, h,
-                       out, n_txt, n_img, d, eps, total);
-  return hipGetLastError();
+#define MOSS_NORM_CASE(N)                                                                                           \
+  if (c4 <= N) {                                                                                                    \
+    hipLaunchKernelGGL(join_mod_rmsnorm_kernel<N>, grid, block, 0, st, x, txt, lens, shift, scale, mod_stride, h,  \
+                       out, n_txt, n_img, d, eps, total);                                                           \
+    return hipGetLastError();                                                                                       \
+  }
+  MOSS_NORM_CASE(4) MOSS_NORM_CASE(8) MOSS_NORM_CASE(12) MOSS_NORM_CASE(16) MOSS_NORM_CASE(32)
+#undef MOSS_NORM_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv(const float* x, const uint16_t* w, float* y, int batch, int d_in, int n_out, hipStream_t st) {
