@@ -290,7 +290,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const uint16_t* _
     __builtin_amdgcn_sched_barrier(0);
   };
   // a matrix step: O^T += V^T P^T for tile t-1, then S^T = K Q^T for tile t
+  // The matrix step runs at raised wavefront priority, so the SIMD issues its MFMAs as soon as the
+  // pipe takes them and the other group's softmax fills the remaining slots (-5 us per block).
   auto pv_qk = [&](int t) {
+    __builtin_amdgcn_s_setprio(1);
     pv(t - 1);
     qk(t);
 #if MOSS_ATTN_SCHED
@@ -302,6 +305,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const uint16_t* _
     }
     __builtin_amdgcn_sched_group_barrier(0x008, MOSS_ATTN_SCHED, 0);
 #endif
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
   };
   // Both groups pass the same n_tiles + 1 workgroup barriers (the first one above).
   if (__builtin_amdgcn_readfirstlane(grp) == 0) {
