@@ -136,6 +136,8 @@ struct Probe {
   int step = -1;
   int max = 0;
   int used = 0;
+  int every = 1;
+  int seen = 0;                // launches of the armed step since arming
   std::vector<hipEvent_t> ev;  // 2 per launch
 };
 Probe g_probe;
@@ -144,6 +146,7 @@ Probe g_probe;
 int probe_begin(int step, hipStream_t st) {
   std::lock_guard<std::mutex> lk(g_probe.mu);
   if (g_probe.step != step || g_probe.used >= g_probe.max) return -1;
+  if (g_probe.seen++ % g_probe.every != 0) return -1;
   const int slot = g_probe.used;
   if (hipEventRecord(g_probe.ev[2 * slot], st) != hipSuccess) return -1;
   g_probe.used = slot + 1;
@@ -731,18 +734,22 @@ int moss_k_gemm_gated_add(int32_t m, int32_t n, int32_t k, const uint16_t* a, in
   return MOSS_OK;
 }
 
-int moss_probe_arm(int32_t step, int32_t max_launches) {
-  if (step < 0 || step >= MOSS_NUM_STEPS || max_launches < 1 || max_launches > 4096) return MOSS_EINVAL;
+int moss_probe_arm(int32_t step, int32_t max_launches, int32_t every) {
+  if (step < 0 || step >= MOSS_NUM_STEPS || max_launches < 1 || max_launches > 4096 || every < 1) return MOSS_EINVAL;
   std::lock_guard<std::mutex> lk(g_probe.mu);
   while ((int)g_probe.ev.size() < 2 * max_launches) {
     hipEvent_t e;
-    const hipError_t err = hipEventCreate(&e);
-    if (err != hipSuccess) return hip_fail(err, "hipEventCreate");
+    // timing only: no system-scope fence (cache writeback and invalidate) at each record, which
+    // left a gap of about 6 us before and after the probed launch
+    const hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableSystemFence);
+    if (err != hipSuccess) return hip_fail(err, "hipEventCreateWithFlags");
     g_probe.ev.push_back(e);
   }
   g_probe.step = step;
   g_probe.max = max_launches;
   g_probe.used = 0;
+  g_probe.every = every;
+  g_probe.seen = 0;
   return MOSS_OK;
 }
 

@@ -84,7 +84,7 @@ _SIGS = {
     "moss_k_gemm_silu": (ctypes.c_int, [c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_i32, c_vp, c_i32, c_vp]),
     "moss_k_gemm_gated_add": (ctypes.c_int, [c_i32, c_i32, c_i32, c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32,
                                              c_vp, c_vp]),
-    "moss_probe_arm": (ctypes.c_int, [c_i32, c_i32]),
+    "moss_probe_arm": (ctypes.c_int, [c_i32, c_i32, c_i32]),
     "moss_probe_collect": (c_i32, [ctypes.POINTER(ctypes.c_float), c_i32]),
 }
 
@@ -314,9 +314,9 @@ def moss_k_gemm_gated_add(m, n, k, a, lda, w, ldw, h, gate, gate_stride, rows_pe
                                        _p(out), _s(stream)), "moss_k_gemm_gated_add")
 
 
-def moss_probe_arm(step, max_launches) -> None:
+def moss_probe_arm(step, max_launches, every: int = 1) -> None:
     s = STEP[step] if isinstance(step, str) else int(step)
-    _check(lib().moss_probe_arm(s, max_launches), "moss_probe_arm")
+    _check(lib().moss_probe_arm(s, max_launches, every), "moss_probe_arm")
 
 
 def moss_probe_collect(max_out: int = 4096) -> list:

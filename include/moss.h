@@ -343,12 +343,15 @@ int moss_k_gated_add(int32_t batch, int32_t rows, int32_t d_model, float* h, con
 #define MOSS_STEP_GATE2 12
 #define MOSS_NUM_STEPS 13
 
-/* Arm the probe: the next up to `max_launches` launches of step `step` by
- * moss_block_forward / moss_stack_forward (any stream, this process) are
- * bracketed by HIP events recorded on the launch stream.  Replaces any
- * earlier arming.  MOSS_EINVAL for a bad step or max_launches outside
- * [1, 4096]; MOSS_EHIP if events cannot be created. */
-int moss_probe_arm(int32_t step, int32_t max_launches);
+/* Arm the probe: from the next launch of step `step` by moss_block_forward /
+ * moss_stack_forward (any stream, this process) on, launches 0, every,
+ * 2 every, ... of that step, up to `max_launches` of them, are bracketed by
+ * HIP events recorded on the launch stream (timing-only events: no
+ * system-scope fence; each record still takes a few microseconds of stream
+ * time, which `every` spreads out).  Replaces any earlier arming.
+ * MOSS_EINVAL for a bad step, max_launches outside [1, 4096] or every < 1;
+ * MOSS_EHIP if events cannot be created. */
+int moss_probe_arm(int32_t step, int32_t max_launches, int32_t every);
 
 /* Disarm, wait for the recorded events and write the duration in ms of each
  * bracketed launch (up to max_out) into ms (host).  Returns the number of

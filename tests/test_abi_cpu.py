@@ -182,9 +182,10 @@ def test_fused_gemm_entry_points_validate():
 
 def test_probe_arguments():
     L = moss.lib()
-    assert L.moss_probe_arm(-1, 4) == moss.MOSS_EINVAL
-    assert L.moss_probe_arm(13, 4) == moss.MOSS_EINVAL
-    assert L.moss_probe_arm(3, 0) == moss.MOSS_EINVAL
+    assert L.moss_probe_arm(-1, 4, 1) == moss.MOSS_EINVAL
+    assert L.moss_probe_arm(13, 4, 1) == moss.MOSS_EINVAL
+    assert L.moss_probe_arm(3, 0, 1) == moss.MOSS_EINVAL
+    assert L.moss_probe_arm(3, 4, 0) == moss.MOSS_EINVAL
     assert L.moss_probe_collect(None, -1) == -moss.MOSS_EINVAL
 
 
