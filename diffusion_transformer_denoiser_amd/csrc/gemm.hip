@@ -32,6 +32,9 @@
 //  * The weight tile is the MFMA's first operand and the activation tile the
 //    second, so a lane's accumulators hold runs of four consecutive output
 //    columns of one row and leave in 8-byte stores.
+//  * Launches with more tiles than CUs run one workgroup per CU, each taking
+//    every G-th tile in turn; its slab ring runs on across its tiles, so a
+//    tile's first slabs are in LDS when the previous tile's epilogue ends.
 // There is no split-K and no atomic: results are identical call to call.
 //
 // Epilogues (the MOSS-Image transformer page's SiLU and gated-add kernels,
@@ -44,6 +47,7 @@
 //  * kGatedAdd (the out and down projections): h[r, :] += gate[b, :] * acc on
 //    the fp32 residual, or, for the last add of a call, out = bf16(h + gate *
 //    acc) with h unchanged.  The projection output is never stored.
+#include <algorithm>
 #include <cmath>
 
 #include "common.h"
@@ -227,13 +231,17 @@ __device__ __forceinline__ void epilogue_qkv(const f32x16 (&acc)[BN / WN / 32][B
       for (int e = 0; e < 16; ++e) sj += acc[i][j][e] * acc[i][j][e];
     ss[j] = sj + __shfl_xor(sj, 32, 64);  // the wavefront's 64 columns of row j*32 + l32
   }
-  float* ss_lds = reinterpret_cast<float*>(smem);  // [wavefront][TM]; the K loop's last reads are done
+  // [wavefront][TM] in a ring stage no load writes before the next tile's first k-step.  The
+  // barriers wait for LDS only: the next tile's slab loads stay in flight.
+  float* ss_lds = reinterpret_cast<float*>(smem);
   if (hh == 0)
 #pragma unroll
     for (int j = 0; j < FM; ++j) ss_lds[wave * TM + j * 32 + l32] = ss[j];
-  __syncthreads();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
   for (int j = 0; j < FM; ++j) ss[j] += ss_lds[(wave ^ 1) * TM + j * 32 + l32];
+  // every partner read done before that stage is loaded again
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   if (which < 2) {
     // gains of this lane's dims half*64 + 32 i + 8 q + 4 hh + e
@@ -319,47 +327,62 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
   static_assert(EPI != kSiluGate || FN % 2 == 0, "the SiLU epilogue pairs gate and up fragments per wavefront");
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * (AB + BB)];
 
-  const int mt = (m - m_begin + BM - 1) / BM;  // this launch covers rows [m_begin, m)
-  int tm, tn;
-  tile_of(blockIdx.x, mt, n / BN, tm, tn);
-  const int m0 = m_begin + tm * BM, n0 = tn * BN;
+  // This launch covers rows [m_begin, m).  Workgroup b computes tiles b, b + G, b + 2G, ... of the
+  // launch (G workgroups); the slab ring runs on from one of its tiles into the next, so the next
+  // tile's first slabs load while this one finishes, and its epilogue's stores drain during the
+  // next tile's first k-steps.
+  const int mt = (m - m_begin + BM - 1) / BM, ntn = n / BN, ntiles = mt * ntn;
+  const int G = gridDim.x;
+  const int mine = (ntiles - (int)blockIdx.x + G - 1) / G;
+  const int nk = k / KB, total = mine * nk;  // slabs this workgroup loads and consumes
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
   const int wm = wave / WN, wn = wave % WN;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
 
   // Load instruction i of wavefront `wave` fills the 1 KiB at (wave + NW*i) of a slab: rows
   // 16*(wave + NW*i) + lane/4, stored slot lane%4, which holds chunk (lane%4) ^ ((row >> 2) & 3).
   // Rows past m are clamped to m - 1; their results are never stored.
-  const uint16_t* ga[LA];
-  const uint16_t* gb[LB];
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
   uint32_t ca[LA];  // LDS byte offset of A chunk i of this wavefront
 #pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    const int chunk = min(wv + NW * i, CA - 1);
-    ca[i] = 1024u * chunk;
-    const int r = chunk * 16 + (lane >> 2);
-    ga[i] = a + (size_t)min(m0 + r, m - 1) * lda + ((lane & 3) ^ ((r >> 2) & 3)) * 8;
-  }
+  for (int i = 0; i < LA; ++i) ca[i] = 1024u * min(wv + NW * i, CA - 1);
+  const uint16_t* ga[LA];
+  const uint16_t* gb[LB];
+  auto aim = [&](int r) {  // point the loads at this workgroup's tile r
+    int tm, tn;
+    tile_of(blockIdx.x + r * G, mt, ntn, tm, tn);
+    const int m0 = m_begin + tm * BM, n0 = tn * BN;
 #pragma unroll
-  for (int i = 0; i < LB; ++i) {
-    const int r = (wave + NW * i) * 16 + (lane >> 2);
-    int wrow = n0 + r;
-    if (EPI == kSiluGate) {
-      // tile row r -> wavefront r / TN, fragment f = (r % TN) / 32: even f = gate rows, odd f = the
-      // up rows of the same outputs
-      const int f = (r % TN) / 32;
-      const int zc = tn * (BN / 2) + (r / TN) * (TN / 2) + (f / 2) * 32 + (r & 31);
-      wrow = ((f & 1) ? n / 2 : 0) + zc;
+    for (int i = 0; i < LA; ++i) {
+      const int rr = min(wv + NW * i, CA - 1) * 16 + (lane >> 2);
+      ga[i] = a + (size_t)min(m0 + rr, m - 1) * lda + ((lane & 3) ^ ((rr >> 2) & 3)) * 8;
     }
-    gb[i] = w + (size_t)wrow * ldw + ((lane & 3) ^ ((r >> 2) & 3)) * 8;
-  }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int rr = (wave + NW * i) * 16 + (lane >> 2);
+      int wrow = n0 + rr;
+      if (EPI == kSiluGate) {
+        // tile row rr -> wavefront rr / TN, fragment f = (rr % TN) / 32: even f = gate rows, odd f =
+        // the up rows of the same outputs
+        const int f = (rr % TN) / 32;
+        const int zc = tn * (BN / 2) + (rr / TN) * (TN / 2) + (f / 2) * 32 + (rr & 31);
+        wrow = ((f & 1) ? n / 2 : 0) + zc;
+      }
+      gb[i] = w + (size_t)wrow * ldw + ((lane & 3) ^ ((rr >> 2) & 3)) * 8;
+    }
+  };
   const uint32_t lds0 = (uint32_t)(uintptr_t)(MOSS_LDS char*)smem;
-  auto issue = [&](int slab) {
-    const uint32_t base = lds0 + (uint32_t)((slab % STAGES) * (AB + BB));
+  int lt = 0, lk = 0, lst = 0;  // the next load: tile, slab within it, ring stage
+  auto issue = [&]() {
+    const uint32_t base = lds0 + (uint32_t)(lst * (AB + BB));
 #pragma unroll
-    for (int i = 0; i < LA; ++i) dma16(ga[i] + slab * KB, base + ca[i]);
+    for (int i = 0; i < LA; ++i) dma16(ga[i] + lk * KB, base + ca[i]);
 #pragma unroll
-    for (int i = 0; i < LB; ++i) dma16(gb[i] + slab * KB, base + AB + 1024u * (wv + NW * i));
+    for (int i = 0; i < LB; ++i) dma16(gb[i] + lk * KB, base + AB + 1024u * (wv + NW * i));
+    if (++lst == STAGES) lst = 0;
+    if (++lk == nk) {
+      lk = 0;
+      if (++lt < mine) aim(lt);
+    }
   };
   // byte offsets of this lane's fragments within a stage, for the two k16 steps of a slab
   int offa[2][FM], offb[2][FN];
@@ -378,8 +401,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
   }
   // reads in the order the k-step's MFMAs first use them (w0 a0 w1 a1 a2 a3 ...; the MFMAs run
   // over the activation fragments in the outer loop), so the first MFMAs' operands arrive first
-  auto ldfrag = [&](int slab, int s, bf16x8* fa, bf16x8* fw) {
-    const char* base = smem + (slab % STAGES) * (AB + BB);
+  auto ldfrag = [&](int stage, int s, bf16x8* fa, bf16x8* fw) {
+    const char* base = smem + stage * (AB + BB);
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       if (j < FN) fw[j] = *reinterpret_cast<const bf16x8*>(base + offb[s][j]);
@@ -389,50 +412,64 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
     for (int i = FM; i < FN; ++i) fw[i] = *reinterpret_cast<const bf16x8*>(base + offb[s][i]);
   };
 
-  f32x16 acc[FN][FM];
-#pragma unroll
-  for (int i = 0; i < FN; ++i)
-#pragma unroll
-    for (int j = 0; j < FM; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  const int nk = k / KB;
+  aim(0);
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p)
-    if (p < nk) issue(p);
+    if (p < total) issue();
   // slabs 0 and 1 resident before the loop (iteration 0 prefetches slab 1)
-  wait_slabs_barrier<PER, STAGES - 3>(min(nk, STAGES - 1) - 2);
+  wait_slabs_barrier<PER, STAGES - 3>(min(total, STAGES - 1) - 2);
 
-  bf16x8 fa0[FM], fw0[FN], fa1[FM], fw1[FN];
-  ldfrag(0, 0, fa0, fw0);
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage (kt+3)%4 held slab kt-1, whose last reads finished before the previous barrier
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
-    ldfrag(kt, 1, fa1, fw1);
+  int g = 0, cs = 0;  // the slab being consumed (counted over this workgroup's tiles) and its stage
+  for (int r = 0; r < mine; ++r) {
+    int tm, tn;
+    tile_of(blockIdx.x + r * G, mt, ntn, tm, tn);
+    const int m0 = m_begin + tm * BM, n0 = tn * BN;
+
+    f32x16 acc[FN][FM];
 #pragma unroll
-    for (int j = 0; j < FM; ++j)
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
-      for (int i = 0; i < FN; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw0[i], fa0[j], acc[i][j], 0, 0, 0);
-    // slab kt+1 is resident; the last iteration re-reads its own stage so the wait counts stay exact
-    ldfrag(kt + 1 < nk ? kt + 1 : kt, 0, fa0, fw0);
+      for (int j = 0; j < FM; ++j)
 #pragma unroll
-    for (int j = 0; j < FM; ++j)
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    bf16x8 fa0[FM], fw0[FN], fa1[FM], fw1[FN];
+    ldfrag(cs, 0, fa0, fw0);
+    for (int kt = 0; kt < nk; ++kt, ++g) {
+      // the stage of slab g-1, whose last reads finished before the previous barrier
+      if (g + STAGES - 1 < total) issue();
+      const int cn = cs + 1 == STAGES ? 0 : cs + 1;
+      ldfrag(cs, 1, fa1, fw1);
 #pragma unroll
-      for (int i = 0; i < FN; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw1[i], fa1[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw0[i], fa0[j], acc[i][j], 0, 0, 0);
+      // slab g+1 is resident; a tile's last k-step re-reads its own stage so the wait counts stay exact
+      ldfrag(kt + 1 < nk ? cn : cs, 0, fa0, fw0);
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw1[i], fa1[j], acc[i][j], 0, 0, 0);
 #if MOSS_GEMM_SCHED
-    // issue each k-step's fragment reads early in the other k-step's MFMAs
-    sched_interleave<MOSS_GEMM_SCHED, FM + FN, FM * FN>();
-    sched_interleave<MOSS_GEMM_SCHED, FM + FN, FM * FN>();
+      // issue each k-step's fragment reads early in the other k-step's MFMAs
+      sched_interleave<MOSS_GEMM_SCHED, FM + FN, FM * FN>();
+      sched_interleave<MOSS_GEMM_SCHED, FM + FN, FM * FN>();
 #endif
-    // slab kt+2 resident for the next iteration (the slabs issued after it may stay in flight)
-    wait_slabs_barrier<PER, STAGES - 3>(min(nk - 1, kt + STAGES - 1) - (kt + 2));
-  }
+      // slab g+2 resident for the next k-step (the slabs issued after it may stay in flight)
+      wait_slabs_barrier<PER, STAGES - 3>(min(total - 1, g + STAGES - 1) - (g + 2));
+      cs = cn;
+    }
 
-  if constexpr (EPI == kQkvPack)
-    epilogue_qkv<BM, BN, WM, WN>(acc, smem, m0, n0, wave, wm, wn, l32, hh, m, ep);
-  else
-    epilogue<BM, BN, WM, WN, EPI>(acc, m0, n0, tn, wm, wn, l32, hh, m, n, c, ldc, ep);
+    if constexpr (EPI == kQkvPack) {
+      // the stage of the tile's last slab stays free until the next tile's first k-step
+      char* spare = smem + (cs == 0 ? STAGES - 1 : cs - 1) * (AB + BB);
+      epilogue_qkv<BM, BN, WM, WN>(acc, spare, m0, n0, wave, wm, wn, l32, hh, m, ep);
+    } else {
+      epilogue<BM, BN, WM, WN, EPI>(acc, m0, n0, tn, wm, wn, l32, hh, m, n, c, ldc, ep);
+    }
+  }
 }
 
 int cu_count() {
@@ -473,8 +510,8 @@ hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_
       const int mt = (m + 255) / 256, rounds = mt * nt / cus, left = mt * nt % cus;
       const int nt1 = rounds * cus / mt, nt2 = nt - nt1, mt2 = (m + 127) / 128;
       if (rounds >= 1 && left > 0 && 2 * left <= cus && nt1 > 0 && nt2 > 0 && mt2 * nt2 <= cus) {
-        hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI, 5>), dim3(mt * nt1), dim3(512), 0, st, a, lda, w, ldw,
-                           c, ldc, 0, m, nt1 * 256, k, ep);
+        hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI, 5>), dim3(std::min(mt * nt1, cus)), dim3(512), 0, st, a,
+                           lda, w, ldw, c, ldc, 0, m, nt1 * 256, k, ep);
         EpiArgs ep2 = ep;
         ep2.col0 = ep.col0 + nt1 * 256;
         hipLaunchKernelGGL((gemm_nt_kernel<128, 256, 2, 4, EPI>), dim3(mt2 * nt2), dim3(512), 0, st, a, lda,
@@ -497,8 +534,9 @@ hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_
         return hipGetLastError();
       }
     }
-    hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI, 5>), dim3(((m_main + 255) / 256) * nt), dim3(512), 0, st,
-                       a, lda, w, ldw, c, ldc, 0, m_main, n, k, ep);
+    // one workgroup per CU, each taking every cus-th tile
+    hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI, 5>), dim3(std::min(((m_main + 255) / 256) * nt, cus)),
+                       dim3(512), 0, st, a, lda, w, ldw, c, ldc, 0, m_main, n, k, ep);
     if (split) {
       // 64 x 128 tiles: twice the workgroups of 64 x 256 ones, so twice the CUs stream the weight
       // panels (the tail is bound by reading all of w once): 50 -> 36 us for the 4096+34-row up
