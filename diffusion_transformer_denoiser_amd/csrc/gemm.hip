@@ -134,6 +134,21 @@ __device__ __forceinline__ void sched_interleave() {
   }
 }
 
+// Lanes l and l ^ 32 hold columns 8q + 4hh + (0..3) of one row, packed as
+// bf16 (`lo` for q = 2p, `hi` for q = 2p + 1).  Trading halves across the
+// two lanes (v_permlane32_swap) leaves lane hh with columns 8(2p + hh) +
+// (0..7): one 16-byte store per lane instead of two 8-byte ones.
+__device__ __forceinline__ u32x4 pair_cols(u32x2 lo, u32x2 hi) {
+  u32x4 r;
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const auto s = __builtin_amdgcn_permlane32_swap(lo[d], hi[d], false, false);
+    r[d] = s[0];
+    r[2 + d] = s[1];
+  }
+  return r;
+}
+
 // acc[i][j] is a 32 x 32 tile of c^T: lane holds row m = l32 of c and
 // columns n = 8q + 4hh + e (e = 0..3) in acc[4q + e].
 template <int BM, int BN, int WM, int WN, int EPI>
@@ -151,13 +166,18 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[BN / WN / 32][BM / 
 #pragma unroll
       for (int pr = 0; pr < FN / 2; ++pr)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = tn * (BN / 2) + wn * (TN / 2) + pr * 32 + 8 * q + 4 * hh;
-          float z[4];
+        for (int p = 0; p < 2; ++p) {
+          u32x2 v[2];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) z[e] = silu_f32(acc[2 * pr][j][4 * q + e]) * acc[2 * pr + 1][j][4 * q + e];
-          u32x2 v = {pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
-          *reinterpret_cast<u32x2*>(crow + col) = v;
+          for (int qq = 0; qq < 2; ++qq) {
+            const int q = 2 * p + qq;
+            float z[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[e] = silu_f32(acc[2 * pr][j][4 * q + e]) * acc[2 * pr + 1][j][4 * q + e];
+            v[qq] = u32x2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+          }
+          const int col = tn * (BN / 2) + wn * (TN / 2) + pr * 32 + 8 * (2 * p + hh);
+          *reinterpret_cast<u32x4*>(crow + col) = pair_cols(v[0], v[1]);
         }
     } else if (EPI == kGatedAdd) {
       const int b = row / ep.rows_per_item;
@@ -186,11 +206,16 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[BN / WN / 32][BM / 
 #pragma unroll
       for (int i = 0; i < FN; ++i) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = n0 + wn * TN + i * 32 + 8 * q + 4 * hh;
-          u32x2 v = {pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                     pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
-          *reinterpret_cast<u32x2*>(crow + col) = v;
+        for (int p = 0; p < 2; ++p) {
+          u32x2 v[2];
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq) {
+            const int q = 2 * p + qq;
+            v[qq] = u32x2{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                          pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+          }
+          const int col = n0 + wn * TN + i * 32 + 8 * (2 * p + hh);
+          *reinterpret_cast<u32x4*>(crow + col) = pair_cols(v[0], v[1]);
         }
       }
     }
@@ -268,25 +293,31 @@ __device__ __forceinline__ void epilogue_qkv(const f32x16 (&acc)[BN / WN / 32][B
       // the 32 lanes of a half wavefront read 32 consecutive rows of it, 256 contiguous bytes
       const float* cr = ep.rope_pp + ((size_t)(half * 16 + hh) * ep.rows_pad + t) * 2;
       const float* sr = cr + (size_t)32 * ep.rows_pad * 2;
-      uint16_t* dst = dbase + (((size_t)b * H + head) * ep.rows_pad + t) * 128 + half * 64 + 4 * hh;
+      uint16_t* dst = dbase + (((size_t)b * H + head) * ep.rows_pad + t) * 128 + half * 64 + 8 * hh;
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const size_t po = (size_t)(8 * i + 2 * q) * ep.rows_pad * 2;  // pair-of-pairs p0 / 2 - (half*16 + hh)
-          const float2 c2 = *reinterpret_cast<const float2*>(cr + po);
-          const float2 s2 = *reinterpret_cast<const float2*>(sr + po);
-          const float cs[2] = {c2.x, c2.y}, sn[2] = {s2.x, s2.y};
-          float o[4];
+        for (int p = 0; p < 2; ++p) {
+          u32x2 v[2];
 #pragma unroll
-          for (int pr = 0; pr < 2; ++pr) {
-            const float x0 = (xr(i, j, 4 * q + 2 * pr) * r) * g[i][q][2 * pr];
-            const float x1 = (xr(i, j, 4 * q + 2 * pr + 1) * r) * g[i][q][2 * pr + 1];
-            o[2 * pr] = x0 * cs[pr] - x1 * sn[pr];
-            o[2 * pr + 1] = x0 * sn[pr] + x1 * cs[pr];
+          for (int qq = 0; qq < 2; ++qq) {
+            const int q = 2 * p + qq;
+            const size_t po = (size_t)(8 * i + 2 * q) * ep.rows_pad * 2;  // pair-of-pairs p0 / 2 - (half*16 + hh)
+            const float2 c2 = *reinterpret_cast<const float2*>(cr + po);
+            const float2 s2 = *reinterpret_cast<const float2*>(sr + po);
+            const float cs[2] = {c2.x, c2.y}, sn[2] = {s2.x, s2.y};
+            float o[4];
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+              const float x0 = (xr(i, j, 4 * q + 2 * pr) * r) * g[i][q][2 * pr];
+              const float x1 = (xr(i, j, 4 * q + 2 * pr + 1) * r) * g[i][q][2 * pr + 1];
+              o[2 * pr] = x0 * cs[pr] - x1 * sn[pr];
+              o[2 * pr + 1] = x0 * sn[pr] + x1 * cs[pr];
+            }
+            v[qq] = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
           }
-          u32x2 v = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-          *reinterpret_cast<u32x2*>(dst + i * 32 + 8 * q) = v;
+          // dims 8 (2p + hh) + (0..7) of this half head
+          *reinterpret_cast<u32x4*>(dst + i * 32 + 16 * p) = pair_cols(v[0], v[1]);
         }
     }
   } else {
