@@ -347,11 +347,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const uint16_t* _
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int dim = 32 * i + 8 * q + 4 * hh;
-        u32x2 v = {pack_bf16x2(acc_o[i][4 * q] * inv, acc_o[i][4 * q + 1] * inv),
-                   pack_bf16x2(acc_o[i][4 * q + 2] * inv, acc_o[i][4 * q + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + dim) = v;
+      for (int p = 0; p < 2; ++p) {
+        u32x2 v[2];
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          const int q = 2 * p + qq;
+          v[qq] = u32x2{pack_bf16x2(acc_o[i][4 * q] * inv, acc_o[i][4 * q + 1] * inv),
+                        pack_bf16x2(acc_o[i][4 * q + 2] * inv, acc_o[i][4 * q + 3] * inv)};
+        }
+        // dims 32 i + 8 (2p + hh) + (0..7)
+        *reinterpret_cast<u32x4*>(orow + 32 * i + 8 * (2 * p + hh)) = pair_cols(v[0], v[1]);
       }
     }
   }

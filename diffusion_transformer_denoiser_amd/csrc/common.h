@@ -44,6 +44,22 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
   return w;
 }
 
+// In the 32x32 MFMA result layout, lanes l and l ^ 32 hold columns 8q + 4hh
+// + (0..3) of one row, packed as bf16 (`lo` for q = 2p, `hi` for q = 2p + 1).
+// Trading halves across the two lanes (v_permlane32_swap) leaves lane hh
+// with columns 8(2p + hh) + (0..7): one 16-byte store per lane instead of two
+// 8-byte ones.
+__device__ __forceinline__ u32x4 pair_cols(u32x2 lo, u32x2 hi) {
+  u32x4 r;
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const auto s = __builtin_amdgcn_permlane32_swap(lo[d], hi[d], false, false);
+    r[d] = s[0];
+    r[2 + d] = s[1];
+  }
+  return r;
+}
+
 // SiLU in fp32, z / (1 + e^-z), from the hardware base-2 exponential and
 // reciprocal (v_exp_f32, v_rcp_f32, about 1 ulp each): five instructions in
 // place of a range-reduced expf and an IEEE division (the up projection's
