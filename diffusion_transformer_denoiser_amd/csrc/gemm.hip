@@ -68,7 +68,7 @@ struct EpiArgs {
   int rows_per_item;  // kGatedAdd, kQkvPack: rows of one item
   uint16_t* out16;    // kGatedAdd: when set, bf16 result here instead of updating h
   // kQkvPack: q/k gains [128], the rotary table re-laid as pairs of pairs (launch_rope_pairs:
-  // rope_pp[cs][pp][t][2] = rope[cs][t][2 pp + 0/1], cs 0 cos / 1 sin, row stride rows_pad), packed outputs
+  // rope_pp[pp][t] = {cos, cos, sin, sin} of pairs 2 pp and 2 pp + 1, row stride rows_pad), packed outputs
   const uint16_t* q_gain;
   const uint16_t* k_gain;
   const float* rope_pp;
@@ -249,6 +249,11 @@ __device__ __forceinline__ void epilogue_gated_lds(const f32x16 (&acc)[BN / WN /
     constexpr int IT = BM / 16;              // row pairs per wavefront
     constexpr int NB = IT % 2 == 0 ? IT / 2 : IT;  // residual loads in flight at once
     const int col = n0 + half * 128 + c4;
+    // the gate row of the tile's item, when all its rows belong to one item
+    const int b0 = m0 / ep.rows_per_item;
+    const bool one_item = b0 == (min(m0 + BM, m) - 1) / ep.rows_per_item;
+    f32x4 g1 = {0.f, 0.f, 0.f, 0.f};
+    if (one_item) g1 = *reinterpret_cast<const f32x4*>(ep.gate + (size_t)b0 * ep.gate_stride + col);
 #pragma unroll
     for (int i0 = 0; i0 < IT; i0 += NB) {
       f32x4 h4[NB];
@@ -261,8 +266,8 @@ __device__ __forceinline__ void epilogue_gated_lds(const f32x16 (&acc)[BN / WN /
       for (int it = 0; it < NB; ++it) {
         const int lr = ((i0 + it) * 8 + wave) * 2 + hh, row = m0 + lr;
         if (row >= m) continue;
-        const float* g = ep.gate + (size_t)(row / ep.rows_per_item) * ep.gate_stride + col;
-        const f32x4 g4 = *reinterpret_cast<const f32x4*>(g);
+        const f32x4 g4 =
+            one_item ? g1 : *reinterpret_cast<const f32x4*>(ep.gate + (size_t)(row / ep.rows_per_item) * ep.gate_stride + col);
         const f32x4 a4 = *reinterpret_cast<const f32x4*>(st + lr * LDR + c4);
         f32x4 o;
 #pragma unroll
@@ -346,10 +351,9 @@ __device__ __forceinline__ void epilogue_qkv(const f32x16 (&acc)[BN / WN / 32][B
       if (row >= m) continue;
       const int b = row / T, t = row - b * T;
       const float r = 1.0f / sqrtf(ss[j] / 128.0f + ep.eps);
-      // pair p0 = half*32 + 16 i + 4 q + 2 hh and p0 + 1: one float2 of the pair-of-pairs table per (i, q);
-      // the 32 lanes of a half wavefront read 32 consecutive rows of it, 256 contiguous bytes
-      const float* cr = ep.rope_pp + ((size_t)(half * 16 + hh) * ep.rows_pad + t) * 2;
-      const float* sr = cr + (size_t)32 * ep.rows_pad * 2;
+      // pairs p0 = half*32 + 16 i + 4 q + 2 hh and p0 + 1: one 16-byte entry of the pair-of-pairs table
+      // per (i, q); the 32 lanes of a half wavefront read 32 consecutive rows of it, 512 contiguous bytes
+      const float* cr = ep.rope_pp + ((size_t)(half * 16 + hh) * ep.rows_pad + t) * 4;
       uint16_t* dst = dbase + (((size_t)b * H + head) * ep.rows_pad + t) * 128 + half * 64 + 8 * hh;
 #pragma unroll
       for (int i = 0; i < FN; ++i)
@@ -359,10 +363,9 @@ __device__ __forceinline__ void epilogue_qkv(const f32x16 (&acc)[BN / WN / 32][B
 #pragma unroll
           for (int qq = 0; qq < 2; ++qq) {
             const int q = 2 * p + qq;
-            const size_t po = (size_t)(8 * i + 2 * q) * ep.rows_pad * 2;  // pair-of-pairs p0 / 2 - (half*16 + hh)
-            const float2 c2 = *reinterpret_cast<const float2*>(cr + po);
-            const float2 s2 = *reinterpret_cast<const float2*>(sr + po);
-            const float cs[2] = {c2.x, c2.y}, sn[2] = {s2.x, s2.y};
+            const size_t po = (size_t)(8 * i + 2 * q) * ep.rows_pad * 4;  // pair-of-pairs p0 / 2 - (half*16 + hh)
+            const f32x4 cs4 = *reinterpret_cast<const f32x4*>(cr + po);
+            const float cs[2] = {cs4[0], cs4[1]}, sn[2] = {cs4[2], cs4[3]};
             float o[4];
 #pragma unroll
             for (int pr = 0; pr < 2; ++pr) {

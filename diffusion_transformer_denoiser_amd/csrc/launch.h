@@ -46,8 +46,9 @@ hipError_t launch_gemm_gated_add(int m, int n, int k, const uint16_t* a, int lda
 // Rows of the packed attention layouts: rows rounded up to a multiple of 128.
 inline int packed_rows(int rows) { return (rows + 127) / 128 * 128; }
 
-// The rotary table [2][rows][64] re-laid as pairs of pairs: rope_pp[cs][pp][t][2] =
-// rope[cs][t][2 pp + 0/1] (32 pp, t < rows, row stride packed_rows(rows)); 512 packed_rows(rows) bytes.
+// The rotary table [2][rows][64] re-laid as pairs of pairs: rope_pp[pp][t][4] = {rope[0][t][2 pp],
+// rope[0][t][2 pp + 1], rope[1][t][2 pp], rope[1][t][2 pp + 1]} (cos, cos, sin, sin; 32 pp, t < rows,
+// row stride packed_rows(rows)); 512 packed_rows(rows) bytes.
 hipError_t launch_rope_pairs(const float* rope, int rows, float* rope_pp, hipStream_t st);
 // The QKV projection of a [batch * rows, 128 n_heads] with a4 in its epilogue: packed Q and K
 // [B, H, T_pad, 128] (normed, gained, rotated with rope_pp from launch_rope_pairs) and V^T

@@ -113,15 +113,21 @@ __global__ __launch_bounds__(256) void zero_packed_pads_kernel(uint16_t* __restr
   }
 }
 
-// rope [2][rows][64] -> rope_pp[cs][pp][t][2] (pairs of pairs, row stride rows_pad); one thread per
-// (cs, pp, t) moves one float2
+// rope [2][rows][64] -> rope_pp[pp][t][4] = cos, cos, sin, sin of pairs 2 pp and 2 pp + 1 (row stride
+// rows_pad); one thread per (pp, t)
+__device__ __forceinline__ void rope_pair_entry(const float* __restrict__ rope, int rows, int rows_pad, long long i,
+                                                float* __restrict__ out) {
+  const long long t = i % rows, pp = i / rows;
+  const float2 c = *reinterpret_cast<const float2*>(rope + t * 64 + 2 * pp);
+  const float2 s = *reinterpret_cast<const float2*>(rope + ((long long)rows + t) * 64 + 2 * pp);
+  *reinterpret_cast<f32x4*>(out + (pp * rows_pad + t) * 4) = f32x4{c.x, c.y, s.x, s.y};
+}
+
 __global__ __launch_bounds__(256) void rope_pairs_kernel(const float* __restrict__ rope, int rows, int rows_pad,
                                                          float* __restrict__ out) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;  // (cs * 32 + pp) * rows + t
-  if (i >= 64 * rows) return;
-  const int t = i % rows, cp = i / rows, cs = cp >> 5, pp = cp & 31;
-  const float2 v = *reinterpret_cast<const float2*>(rope + ((size_t)cs * rows + t) * 64 + 2 * pp);
-  *reinterpret_cast<float2*>(out + ((size_t)cp * rows_pad + t) * 2) = v;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;  // pp * rows + t
+  if (i >= 32 * rows) return;
+  rope_pair_entry(rope, rows, rows_pad, i, out);
 }
 
 // The once-per-call preparation of a block stack in one launch: SiLU(cond)
@@ -133,16 +139,13 @@ __global__ __launch_bounds__(256) void call_prologue_kernel(const uint16_t* __re
                                                             int rows_pad, float* __restrict__ rope_pp,
                                                             uint16_t* __restrict__ q, uint16_t* __restrict__ k,
                                                             uint16_t* __restrict__ v, int n_bh) {
-  const long long n1 = n_cond, n2 = 64LL * rows, npad = rows_pad - rows, n3 = npad * 128 * n_bh;
+  const long long n1 = n_cond, n2 = 32LL * rows, npad = rows_pad - rows, n3 = npad * 128 * n_bh;
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n1 + n2 + n3;
        i += (long long)gridDim.x * blockDim.x) {
     if (i < n1) {
       s[i] = silu_f32(bf16_to_f32(cond[i]));
     } else if (i < n1 + n2) {
-      const long long j = i - n1;  // (cs * 32 + pp) * rows + t
-      const long long t = j % rows, cp = j / rows, cs = cp >> 5, pp = cp & 31;
-      const float2 val = *reinterpret_cast<const float2*>(rope + (cs * rows + t) * 64 + 2 * pp);
-      *reinterpret_cast<float2*>(rope_pp + (cp * rows_pad + t) * 2) = val;
+      rope_pair_entry(rope, rows, rows_pad, i - n1, rope_pp);  // pp * rows + t
     } else {
       const long long j = i - n1 - n2, per = npad * 128;
       const long long bh = j / per, r = j - bh * per;
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(256) void call_prologue_kernel(const uint16_t* __re
 hipError_t launch_call_prologue(const uint16_t* cond, float* s, int n_cond, const float* rope, int batch, int rows,
                                 int n_heads, float* rope_pp, uint16_t* q, uint16_t* k, uint16_t* v, hipStream_t st) {
   const int rp = packed_rows(rows);
-  const long long total = (long long)n_cond + 64LL * rows + (long long)(rp - rows) * 128 * batch * n_heads;
+  const long long total = (long long)n_cond + 32LL * rows + (long long)(rp - rows) * 128 * batch * n_heads;
   const int blocks = (int)std::min<long long>((total + 255) / 256, 2048);
   hipLaunchKernelGGL(call_prologue_kernel, dim3(blocks), dim3(256), 0, st, cond, s, n_cond, rope, rows, rp, rope_pp,
                      q, k, v, batch * n_heads);
@@ -167,7 +170,7 @@ hipError_t launch_call_prologue(const uint16_t* cond, float* s, int n_cond, cons
 }
 
 hipError_t launch_rope_pairs(const float* rope, int rows, float* rope_pp, hipStream_t st) {
-  hipLaunchKernelGGL(rope_pairs_kernel, dim3((64 * rows + 255) / 256), dim3(256), 0, st, rope, rows,
+  hipLaunchKernelGGL(rope_pairs_kernel, dim3((32 * rows + 255) / 256), dim3(256), 0, st, rope, rows,
                      packed_rows(rows), rope_pp);
   return hipGetLastError();
 }
