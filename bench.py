@@ -118,10 +118,9 @@ def traffic_summary(fetch_dir, write_dir, geom):
     per = {}
     for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = read_counter_csv(folder, counter)
-        # the 4130-row up projection's dispatches: 1536 whole tiles of 512 threads, 192 tail tiles of 256
-        grids = (1536 * 512, 192 * 256)
-        parts = [[v for name, grid, v in rows if kname in name and grid == gsz]
-                 for kname, gsz in zip(UP_KERNELS, grids)]
+        # the up projection's dispatches (its two kernels run nowhere else in a block forward): the
+        # whole 256-row tiles, one workgroup per CU, then the 192 tail tiles of 64 x 128
+        parts = [[v for name, grid, v in rows if kname in name] for kname in UP_KERNELS]
         copies = [v for name, _, v in rows if "copyBuffer" in name]
         if not parts[0] or not copies:
             raise SystemExit(f"{counter}: no up-projection dispatch or no copy dispatch in {folder}")
