@@ -100,7 +100,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const uint16_t* _
                                                                float scale_log2) {
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStage];
 
-  const int qt = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
+  // Workgroup ids are dealt round-robin over the 8 XCDs; remap them so each XCD runs a contiguous
+  // stretch of the (item, head, query tile) order: the query tiles of a head then share their
+  // XCD's L2, and its K/V tiles are fetched into one L2 rather than all eight.
+  const int nqt = gridDim.x, nblk = nqt * gridDim.y * gridDim.z;
+  const int id = blockIdx.x + nqt * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int per = nblk / 8, rem = nblk % 8, x = id % 8, l = id / 8;
+  const int logical = (x < rem) ? x * (per + 1) + l : rem * (per + 1) + (x - rem) * per + l;
+  const int qt = logical % nqt, head = (logical / nqt) % n_heads, b = logical / (nqt * n_heads);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
   const size_t bh = (size_t)b * n_heads + head;
   const uint16_t* qb = qp + bh * rows_pad * 128;
