@@ -5,6 +5,8 @@
 // the modulated RMSNorm, SiLU and gated-add kernels and the precision policy
 // (bf16 storage, fp32 sums and norms).  Every kernel here moves 16 bytes per
 // lane per access (eight bf16) so that a wavefront touches 1 KiB contiguous.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -37,6 +39,12 @@ __global__ __launch_bounds__(kThreads) void join_rows_kernel(const u32x4* __rest
 }
 
 // ---- a1: s = SiLU(cond) in fp32, then mod = W_mod s -------------------------
+constexpr int kGemvSet = 32;  // weight matrices one modulation launch takes
+struct GemvSet {
+  const uint16_t* w[kGemvSet];  // [6 d, d] bf16 each
+  unsigned skip[kGemvSet];      // items whose gates that matrix's output zeroes
+};
+
 __global__ __launch_bounds__(kThreads) void silu_cond_kernel(const uint16_t* __restrict__ cond,
                                                              float* __restrict__ s, int n) {
   const int i = blockIdx.x * kThreads + threadIdx.x;
@@ -47,14 +55,19 @@ __global__ __launch_bounds__(kThreads) void silu_cond_kernel(const uint16_t* __r
 // Lane l takes the 16-byte chunks l, l + 64, ... of the row (CPL of them at
 // most) and issues all its weight loads before any arithmetic, so a
 // wavefront has its whole row in flight at once (the row is read once).
+// blockIdx.y picks one of up to kGemvSet weight matrices (the modulations of
+// a whole block stack depend only on cond, so one launch computes them all
+// and streams every block's W_mod back to back).
 template <int CPL>
-__global__ __launch_bounds__(kThreads) void adaln_gemv_kernel(const float* __restrict__ s,
-                                                              const uint16_t* __restrict__ w,
+__global__ __launch_bounds__(kThreads) void adaln_gemv_kernel(const float* __restrict__ s, GemvSet set,
                                                               float* __restrict__ mod, int batch, int n_out,
-                                                              int d, unsigned skip_items) {
+                                                              int d) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (row >= n_out) return;
+  const uint16_t* __restrict__ w = set.w[blockIdx.y];
+  const unsigned skip_items = set.skip[blockIdx.y];
+  mod += (size_t)blockIdx.y * batch * n_out;
   const u32x4* wr = reinterpret_cast<const u32x4*>(w + (size_t)row * d);
   const int nch = d >> 3;
   u32x4 wv[CPL];
@@ -330,22 +343,45 @@ hipError_t launch_silu_cond(const uint16_t* cond, float* s, int batch, int d, hi
   return hipGetLastError();
 }
 
+// y[m][b][:n_out] = W_m x[b] for the set's matrices m < n_mats (each [n_out, d_in] bf16)
+static hipError_t launch_gemv_set(const float* x, const GemvSet& set, int n_mats, float* y, int batch, int d_in,
+                                  int n_out, hipStream_t st) {
+  const int cpl = (d_in / 8 + 63) / 64;
+  const dim3 grid((n_out + 3) / 4, n_mats), block(kThreads);
+  if (cpl <= 2)
+    hipLaunchKernelGGL(adaln_gemv_kernel<2>, grid, block, 0, st, x, set, y, batch, n_out, d_in);
+  else if (cpl <= 4)
+    hipLaunchKernelGGL(adaln_gemv_kernel<4>, grid, block, 0, st, x, set, y, batch, n_out, d_in);
+  else if (cpl <= 6)
+    hipLaunchKernelGGL(adaln_gemv_kernel<6>, grid, block, 0, st, x, set, y, batch, n_out, d_in);
+  else if (cpl <= 8)
+    hipLaunchKernelGGL(adaln_gemv_kernel<8>, grid, block, 0, st, x, set, y, batch, n_out, d_in);
+  else
+    hipLaunchKernelGGL(adaln_gemv_kernel<16>, grid, block, 0, st, x, set, y, batch, n_out, d_in);
+  return hipGetLastError();
+}
+
 hipError_t launch_adaln_gemv(const float* s, const uint16_t* w_mod, float* mod, int batch, int d, unsigned skip_items,
                              hipStream_t st) {
-  const int n_out = 6 * d;
-  const int cpl = (d / 8 + 63) / 64;
-  const dim3 grid((n_out + 3) / 4), block(kThreads);
-  if (cpl <= 2)
-    hipLaunchKernelGGL(adaln_gemv_kernel<2>, grid, block, 0, st, s, w_mod, mod, batch, n_out, d, skip_items);
-  else if (cpl <= 4)
-    hipLaunchKernelGGL(adaln_gemv_kernel<4>, grid, block, 0, st, s, w_mod, mod, batch, n_out, d, skip_items);
-  else if (cpl <= 6)
-    hipLaunchKernelGGL(adaln_gemv_kernel<6>, grid, block, 0, st, s, w_mod, mod, batch, n_out, d, skip_items);
-  else if (cpl <= 8)
-    hipLaunchKernelGGL(adaln_gemv_kernel<8>, grid, block, 0, st, s, w_mod, mod, batch, n_out, d, skip_items);
-  else
-    hipLaunchKernelGGL(adaln_gemv_kernel<16>, grid, block, 0, st, s, w_mod, mod, batch, n_out, d, skip_items);
-  return hipGetLastError();
+  GemvSet set{};
+  set.w[0] = w_mod;
+  set.skip[0] = skip_items;
+  return launch_gemv_set(s, set, 1, mod, batch, d, 6 * d, st);
+}
+
+hipError_t launch_adaln_gemv_many(const float* s, const uint16_t* const* w_mods, const unsigned* skip, int n,
+                                  float* mod, int batch, int d, hipStream_t st) {
+  for (int i0 = 0; i0 < n; i0 += kGemvSet) {
+    GemvSet set{};
+    const int k = std::min(kGemvSet, n - i0);
+    for (int i = 0; i < k; ++i) {
+      set.w[i] = w_mods[i0 + i];
+      set.skip[i] = skip[i0 + i];
+    }
+    const hipError_t e = launch_gemv_set(s, set, k, mod + (size_t)i0 * batch * 6 * d, batch, d, 6 * d, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_mod_rmsnorm(const float* h, const float* shift, const float* scale, int mod_stride,
@@ -414,19 +450,9 @@ hipError_t launch_join_mod_rmsnorm(const uint16_t* x, const uint16_t* txt, const
 }
 
 hipError_t launch_gemv(const float* x, const uint16_t* w, float* y, int batch, int d_in, int n_out, hipStream_t st) {
-  const int cpl = (d_in / 8 + 63) / 64;
-  const dim3 grid((n_out + 3) / 4), block(kThreads);
-  if (cpl <= 2)
-    hipLaunchKernelGGL(adaln_gemv_kernel<2>, grid, block, 0, st, x, w, y, batch, n_out, d_in, 0u);
-  else if (cpl <= 4)
-    hipLaunchKernelGGL(adaln_gemv_kernel<4>, grid, block, 0, st, x, w, y, batch, n_out, d_in, 0u);
-  else if (cpl <= 6)
-    hipLaunchKernelGGL(adaln_gemv_kernel<6>, grid, block, 0, st, x, w, y, batch, n_out, d_in, 0u);
-  else if (cpl <= 8)
-    hipLaunchKernelGGL(adaln_gemv_kernel<8>, grid, block, 0, st, x, w, y, batch, n_out, d_in, 0u);
-  else
-    hipLaunchKernelGGL(adaln_gemv_kernel<16>, grid, block, 0, st, x, w, y, batch, n_out, d_in, 0u);
-  return hipGetLastError();
+  GemvSet set{};
+  set.w[0] = w;
+  return launch_gemv_set(x, set, 1, y, batch, d_in, n_out, st);
 }
 
 hipError_t launch_timestep_features(const ItemTimes& ts, float* f, int batch, hipStream_t st) {

@@ -14,6 +14,10 @@ hipError_t launch_silu_cond(const uint16_t* cond, float* s, int batch, int d, hi
 // mod = W_mod s per item; items whose bit is set in skip_items get zero gate1 and gate2.
 hipError_t launch_adaln_gemv(const float* s, const uint16_t* w_mod, float* mod, int batch, int d, unsigned skip_items,
                              hipStream_t st);
+// The modulations of n blocks in as few launches as possible: mod [n][batch][6 d] fp32, block i from
+// w_mods[i] with the gates of the items in skip[i] zeroed.
+hipError_t launch_adaln_gemv_many(const float* s, const uint16_t* const* w_mods, const unsigned* skip, int n,
+                                  float* mod, int batch, int d, hipStream_t st);
 // join_rows into h (fp32) and the first modulated RMSNorm into out (bf16) in one pass.
 hipError_t launch_join_mod_rmsnorm(const uint16_t* x, const uint16_t* txt, const ItemLens& lens, const float* shift,
                                    const float* scale, int mod_stride, float* h, uint16_t* out, int batch, int n_txt,

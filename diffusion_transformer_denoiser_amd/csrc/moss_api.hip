@@ -72,7 +72,7 @@ struct Layout {
 // output reaches memory as such: QKV is normed, rotated and packed in its
 // epilogue, the out and down projections add into h in theirs, and the up
 // projection applies the SiLU gate in its own.
-Layout plan(const moss_dims* d) {
+Layout plan(const moss_dims* d, int n_blocks) {
   Layout L;
   const size_t B = d->batch, T = (size_t)d->n_txt + d->n_img, D = d->d_model, F = d->mlp_inner;
   const size_t R = B * T, Tp = packed_rows((int)T), H = d->n_heads;
@@ -83,7 +83,7 @@ Layout plan(const moss_dims* d) {
     return o;
   };
   L.s_cond = take(4 * B * D);
-  L.mod = take(4 * B * 6 * D);
+  L.mod = take(4 * B * 6 * D * (size_t)n_blocks);  // every block's modulation, computed up front
   L.h = take(4 * R * D);
   L.a = take(2 * R * D);
   const size_t packed = 2 * B * H * Tp * 128;
@@ -182,14 +182,13 @@ struct FirstRows {
   const uint16_t* txt;
 };
 
-// Items whose bit is set in skip_items get zero gates, so the block leaves their residual unchanged.
+// mod: this block's modulation [B][6 D] (computed for the whole stack up front; items a block skips
+// have zero gates there, so the block leaves their residual unchanged).
 int run_block(const Ctx& c, const moss_block_weights* w, const float* rope, float* h, uint16_t* out16,
-              unsigned skip_items, const FirstRows* first) {
+              const float* mod, const FirstRows* first) {
   const moss_dims* d = c.d;
   const int B = d->batch, T = d->n_txt + d->n_img, D = d->d_model, F = d->mlp_inner, H = d->n_heads;
   const int R = B * T;
-  float* s = reinterpret_cast<float*>(c.ws + c.L.s_cond);
-  float* mod = reinterpret_cast<float*>(c.ws + c.L.mod);
   uint16_t* a = reinterpret_cast<uint16_t*>(c.ws + c.L.a);
   uint16_t* qp = reinterpret_cast<uint16_t*>(c.ws + c.L.qp);
   uint16_t* kp = reinterpret_cast<uint16_t*>(c.ws + c.L.kp);
@@ -197,10 +196,6 @@ int run_block(const Ctx& c, const moss_block_weights* w, const float* rope, floa
   uint16_t* z = reinterpret_cast<uint16_t*>(c.ws + c.L.z);
   const int ms = 6 * D;  // item stride of the modulation vector
   hipStream_t st = c.st;
-  {
-    StepTimer t(MOSS_STEP_ADALN, st);
-    MOSS_TRY(launch_adaln_gemv(s, w->w_mod, mod, B, D, skip_items, st), "adaln_gemv");
-  }
   if (first) {
     StepTimer t(MOSS_STEP_JOIN, st);  // row join + the first norm, one pass
     MOSS_TRY(launch_join_mod_rmsnorm(first->x, first->txt, c.lens, mod + 0 * D, mod + 1 * D, ms, h, a, B, d->n_txt,
@@ -261,7 +256,7 @@ int validate_forward(const moss_dims* d, int n_blocks, const uint16_t* x, const 
   for (int i = 0; i < n_blocks; ++i)
     if (!weights_ok(&blocks[i])) return MOSS_EINVAL;
   if (!workspace || !aligned16(workspace)) return MOSS_EWORKSPACE;
-  ctx->L = plan(d);
+  ctx->L = plan(d, n_blocks);
   if (ws_bytes < ctx->L.total) return MOSS_EWORKSPACE;
   const size_t B = d->batch, T = (size_t)d->n_txt + d->n_img, D = d->d_model, F = d->mlp_inner;
   const size_t out_bytes = 2 * B * T * D;
@@ -298,13 +293,27 @@ int run_stack(const Ctx& c, int n_blocks, const uint16_t* x, const uint16_t* txt
                                 reinterpret_cast<uint16_t*>(c.ws + c.L.kp),
                                 reinterpret_cast<uint16_t*>(c.ws + c.L.vp), c.st),
            "call prologue");
+  // every block's modulation depends only on cond: one launch streams all the W_mod matrices
+  float* mod = reinterpret_cast<float*>(c.ws + c.L.mod);
+  const size_t mod_stride = (size_t)d->batch * 6 * d->d_model;
+  {
+    std::vector<const uint16_t*> w_mods(n_blocks);
+    std::vector<unsigned> masks(n_blocks, 0u);
+    for (int i = 0; i < n_blocks; ++i) {
+      w_mods[i] = blocks[i].w_mod;
+      if (skip)
+        for (int b = 0; b < d->batch; ++b)
+          if (skip[(size_t)i * d->batch + b]) masks[i] |= 1u << b;
+    }
+    StepTimer t(MOSS_STEP_ADALN, c.st);
+    MOSS_TRY(launch_adaln_gemv_many(reinterpret_cast<const float*>(c.ws + c.L.s_cond), w_mods.data(), masks.data(),
+                                    n_blocks, mod, d->batch, d->d_model, c.st),
+             "adaln_gemv");
+  }
   for (int i = 0; i < n_blocks; ++i) {
-    unsigned mask = 0;
-    if (skip)
-      for (int b = 0; b < d->batch; ++b)
-        if (skip[(size_t)i * d->batch + b]) mask |= 1u << b;
     const FirstRows rows{x, txt};
-    const int rc = run_block(c, &blocks[i], rope, h, i + 1 == n_blocks ? out : nullptr, mask, i == 0 ? &rows : nullptr);
+    const int rc = run_block(c, &blocks[i], rope, h, i + 1 == n_blocks ? out : nullptr, mod + i * mod_stride,
+                             i == 0 ? &rows : nullptr);
     if (rc != MOSS_OK) return rc;
   }
   return MOSS_OK;
@@ -377,7 +386,7 @@ int denoiser(const moss_dims* d, int n_blocks, const uint16_t* latent, const uin
   for (int i = 0; i < n_blocks; ++i)
     if (!weights_ok(&blocks[i])) return MOSS_EINVAL;
   if (!workspace || !aligned16(workspace)) return MOSS_EWORKSPACE;
-  c.L = plan(d);
+  c.L = plan(d, n_blocks);
   const EndsLayout E = plan_ends(d, c.L.total);
   if (ws_bytes < E.total) return MOSS_EWORKSPACE;
   const size_t B = d->batch, T = (size_t)d->n_txt + d->n_img, D = d->d_model, F = d->mlp_inner;
@@ -460,7 +469,7 @@ int moss_device_check(int hip_device) { return check_device(hip_device); }
 
 size_t moss_workspace_bytes(const moss_dims* dims, int32_t n_blocks) {
   if (!dims_ok(dims) || n_blocks < 1) return 0;
-  return plan(dims).total;
+  return plan(dims, n_blocks).total;
 }
 
 int32_t moss_packed_rows(int32_t rows) { return rows < 1 ? 0 : packed_rows(rows); }
@@ -496,7 +505,7 @@ int moss_stack_forward_skip(const moss_dims* dims, int32_t n_blocks, const uint1
 
 size_t moss_denoiser_workspace_bytes(const moss_dims* dims, int32_t n_blocks) {
   if (!dims_ok(dims) || n_blocks < 1 || dims->n_img < 1) return 0;
-  return plan_ends(dims, plan(dims).total).total;
+  return plan_ends(dims, plan(dims, n_blocks).total).total;
 }
 
 int moss_denoiser_forward(const moss_dims* dims, int32_t n_blocks, const uint16_t* latent, const uint16_t* enc,

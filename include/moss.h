@@ -86,10 +86,11 @@ const char* moss_status_string(int status);
 int moss_device_check(int hip_device);
 
 /* Bytes of device workspace one moss_block_forward / moss_stack_forward call
- * with these dims needs (n_blocks >= 1; 1 for moss_block_forward).  Returns 0
- * when the dims are invalid.  One plan serves every call whose dims are no
- * larger, as the CUDA port page's `fit` plans one scratch for every geometry
- * (TensorFold PR #2281, "What this changes"). */
+ * with these dims needs (n_blocks >= 1; 1 for moss_block_forward; every
+ * block's modulation is computed up front, so it grows by 24 B D per block).
+ * Returns 0 when the dims are invalid.  One plan serves every call whose dims
+ * and block count are no larger, as the CUDA port page's `fit` plans one
+ * scratch for every geometry (TensorFold PR #2281, "What this changes"). */
 size_t moss_workspace_bytes(const moss_dims* dims, int32_t n_blocks);
 
 /* Fill the 2D axial rotary tables rope[2][T][64] (fp32, device): cos, then

@@ -65,7 +65,8 @@ def test_workspace_bytes():
     ws = moss.moss_workspace_bytes(d, 1)
     # fp32 residual (50.7 MB) + a (25.4 MB) + packed q/k/v (3 x 26.0 MB) + z (101.5 MB)
     assert 250 * MB < ws < 260 * MB, ws
-    assert moss.moss_workspace_bytes(d, 24) == ws
+    # every block's modulation [B, 6D] fp32 is computed up front: 73.7 KB more per block at B = 1
+    assert moss.moss_workspace_bytes(d, 24) - ws == 23 * 4 * 6 * 3072
     assert moss.moss_workspace_bytes(c2_dims(batch=2), 1) > ws
     assert moss.moss_workspace_bytes(c2_dims(head_dim=64), 1) == 0
     assert moss.moss_workspace_bytes(d, 0) == 0
