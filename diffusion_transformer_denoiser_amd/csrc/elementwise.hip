@@ -113,12 +113,41 @@ __global__ __launch_bounds__(kThreads) void adaln_gemv_kernel(const float* __res
 // load or store instruction of a wavefront covers one contiguous stretch of the row (1 KiB of
 // fp32, 512 B of bf16).  The shift and scale of a chunk are loaded where they are used, which
 // keeps the register count (and so the wavefronts in flight per SIMD) up.
+// Lanes l and l ^ 1 trade one 8-byte half (DPP quad_perm [1, 0, 3, 2]).
+__device__ __forceinline__ u32x2 swap_neighbour(u32x2 x) {
+  return u32x2{(uint32_t)__builtin_amdgcn_mov_dpp((int)x[0], 0xB1, 0xF, 0xF, false),
+               (uint32_t)__builtin_amdgcn_mov_dpp((int)x[1], 0xB1, 0xF, 0xF, false)};
+}
+
 template <int C4>
 __device__ __forceinline__ void modulate_store(const f32x4 (&v)[C4], float ss, const float* __restrict__ sh,
                                                 const float* __restrict__ sc, uint16_t* __restrict__ dst, int lane,
                                                 int nch4, int d, float eps) {
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)d + eps);
+  auto mod4 = [&](const f32x4& x, int c) {
+    const f32x4 shv = reinterpret_cast<const f32x4*>(sh)[c];
+    const f32x4 scv = reinterpret_cast<const f32x4*>(sc)[c];
+    float o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = (x[j] * r) * (1.0f + scv[j]) + shv[j];
+    return u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+  };
+  if (C4 % 2 == 0 && nch4 == 64 * C4) {
+    // whole chunk pairs: for chunks i and i + 1, an even lane stores its own and its odd
+    // neighbour's values of chunk i, the odd lane both lanes' values of chunk i + 1 (8
+    // consecutive values, 16 bytes each): half the store instructions
+    const bool odd = lane & 1;
+#pragma unroll
+    for (int i = 0; i < C4; i += 2) {
+      const u32x2 p0 = mod4(v[i], lane + 64 * i), p1 = mod4(v[i + 1], lane + 64 * (i + 1));
+      const u32x2 got = swap_neighbour(odd ? p0 : p1);
+      const u32x4 o = odd ? u32x4{got[0], got[1], p1[0], p1[1]} : u32x4{p0[0], p0[1], got[0], got[1]};
+      const int e = 4 * ((lane & ~1) + 64 * (odd ? i + 1 : i));
+      *reinterpret_cast<u32x4*>(dst + e) = o;
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < C4; ++i) {
     const int c = lane + 64 * i;
@@ -177,15 +206,38 @@ __global__ __launch_bounds__(kThreads) void join_mod_rmsnorm_kernel(
   f32x4 v[C4];
   float ss = 0.0f;
   f32x4* hrow = reinterpret_cast<f32x4*>(h + (size_t)row * d);
+  auto widen = [](u32x2 w) { return f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])}; };
+  if (C4 % 2 == 0 && nch4 == 64 * C4) {
+    // whole chunk pairs, loaded 16 bytes per lane as modulate_store stores them: an even lane
+    // reads chunk i of itself and its odd neighbour, the odd lane chunk i + 1 of both, and the
+    // two trade the halves that belong to the other
+    const bool odd = lane & 1;
+    const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
 #pragma unroll
-  for (int i = 0; i < C4; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nch4) {
-      const u32x2 w = src ? src[c] : u32x2{0u, 0u};
-      v[i] = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
-      hrow[c] = v[i];
+    for (int i = 0; i < C4; i += 2) {
+      const u32x4 q = src ? src4[((lane & ~1) + 64 * (odd ? i + 1 : i)) >> 1] : u32x4{0u, 0u, 0u, 0u};
+      const u32x2 lo = {q[0], q[1]}, hi = {q[2], q[3]};
+      const u32x2 got = swap_neighbour(odd ? lo : hi);
+      v[i] = widen(odd ? got : lo);
+      v[i + 1] = widen(odd ? hi : got);
+    }
+#pragma unroll
+    for (int i = 0; i < C4; ++i) {
+      hrow[lane + 64 * i] = v[i];
 #pragma unroll
       for (int j = 0; j < 4; ++j) ss += v[i][j] * v[i][j];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < C4; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nch4) {
+        const u32x2 w = src ? src[c] : u32x2{0u, 0u};
+        v[i] = widen(w);
+        hrow[c] = v[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ss += v[i][j] * v[i][j];
+      }
     }
   }
   modulate_store<C4>(v, ss, shift + (size_t)b * mod_stride, scale + (size_t)b * mod_stride, out + (size_t)row * d,
