@@ -58,17 +58,22 @@ __global__ __launch_bounds__(kThreads) void silu_cond_kernel(const uint16_t* __r
 // blockIdx.y picks one of up to kGemvSet weight matrices (the modulations of
 // a whole block stack depend only on cond, so one launch computes them all
 // and streams every block's W_mod back to back).
+// s is read by every row: with kGemvRows wavefronts per workgroup, one copy of it goes into LDS
+// (when it fits) rather than each wavefront reading its own from L2.
+constexpr int kGemvRows = 8;                  // wavefronts (rows) per workgroup
+constexpr int kGemvLdsFloats = 8192;          // s staged in LDS up to 32 KiB (batch * d floats)
 template <int CPL>
-__global__ __launch_bounds__(kThreads) void adaln_gemv_kernel(const float* __restrict__ s, GemvSet set,
-                                                              float* __restrict__ mod, int batch, int n_out,
-                                                              int d) {
+__global__ __launch_bounds__(64 * kGemvRows) void adaln_gemv_kernel(const float* __restrict__ s, GemvSet set,
+                                                                    float* __restrict__ mod, int batch, int n_out,
+                                                                    int d) {
+  __shared__ __attribute__((aligned(16))) float s_lds[kGemvLdsFloats];
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (row >= n_out) return;
+  const int row = blockIdx.x * kGemvRows + (threadIdx.x >> 6);
+  const bool live = row < n_out;
   const uint16_t* __restrict__ w = set.w[blockIdx.y];
   const unsigned skip_items = set.skip[blockIdx.y];
   mod += (size_t)blockIdx.y * batch * n_out;
-  const u32x4* wr = reinterpret_cast<const u32x4*>(w + (size_t)row * d);
+  const u32x4* wr = reinterpret_cast<const u32x4*>(w + (size_t)min(row, n_out - 1) * d);
   const int nch = d >> 3;
   u32x4 wv[CPL];
 #pragma unroll
@@ -76,6 +81,15 @@ __global__ __launch_bounds__(kThreads) void adaln_gemv_kernel(const float* __res
     const int c = lane + 64 * i;
     wv[i] = c < nch ? wr[c] : u32x4{0u, 0u, 0u, 0u};
   }
+  const bool staged = batch * d <= kGemvLdsFloats;
+  if (staged) {
+    // the weight loads are in flight; copy s meanwhile
+    for (int k = threadIdx.x; k < batch * d / 4; k += 64 * kGemvRows)
+      reinterpret_cast<f32x4*>(s_lds)[k] = reinterpret_cast<const f32x4*>(s)[k];
+    __syncthreads();
+  }
+  const float* sv = staged ? s_lds : s;
+  if (!live) return;
   float acc[MOSS_MAX_BATCH];
 #pragma unroll
   for (int b = 0; b < MOSS_MAX_BATCH; ++b) acc[b] = 0.0f;
@@ -88,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void adaln_gemv_kernel(const float* __res
 #pragma unroll
       for (int b = 0; b < MOSS_MAX_BATCH; ++b) {
         if (b < batch) {
-          const f32x4* sp = reinterpret_cast<const f32x4*>(s + (size_t)b * d + 8 * c);
+          const f32x4* sp = reinterpret_cast<const f32x4*>(sv + (size_t)b * d + 8 * c);
           const f32x4 s0 = sp[0], s1 = sp[1];
           acc[b] += f[0] * s0[0] + f[1] * s0[1] + f[2] * s0[2] + f[3] * s0[3] + f[4] * s1[0] +
                     f[5] * s1[1] + f[6] * s1[2] + f[7] * s1[3];
@@ -399,7 +413,7 @@ hipError_t launch_silu_cond(const uint16_t* cond, float* s, int batch, int d, hi
 static hipError_t launch_gemv_set(const float* x, const GemvSet& set, int n_mats, float* y, int batch, int d_in,
                                   int n_out, hipStream_t st) {
   const int cpl = (d_in / 8 + 63) / 64;
-  const dim3 grid((n_out + 3) / 4, n_mats), block(kThreads);
+  const dim3 grid((n_out + kGemvRows - 1) / kGemvRows, n_mats), block(64 * kGemvRows);
   if (cpl <= 2)
     hipLaunchKernelGGL(adaln_gemv_kernel<2>, grid, block, 0, st, x, set, y, batch, n_out, d_in);
   else if (cpl <= 4)
