@@ -67,9 +67,6 @@ constexpr int BKV = 64;          // keys per tile
 constexpr int kThreads = 64 * NWV;
 constexpr int kStage = 32768;    // K tile (16 KiB) then V^T tile (16 KiB)
 constexpr int kStages = 3;       // K/V tiles in LDS
-#ifndef MOSS_ATTN_MSUM
-#define MOSS_ATTN_MSUM 0
-#endif
 constexpr float kLazy = 8.0f;  // log2-unit growth of a row max that forces a rescale
 
 // Row r of a 32-key block of S^T holds key quad_swap(r): quads 1 and 2 of
@@ -170,18 +167,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const uint16_t* _
     for (int e = 0; e < 16; ++e) acc_o[i][e] = 0.0f;
   float m_use = -INFINITY;  // max (log2 units, scaled) the exponentials are taken against
   float l_run = 0.0f;
-#if MOSS_ATTN_MSUM
-  // The row sums of the probabilities come out of the PV product: a first
-  // operand whose row 0 is all ones gives, in row 0 of its accumulator, the
-  // sum over the tile's keys of each query's bf16 probabilities (lanes 0-31
-  // hold row 0; the other rows stay zero).
-  f32x16 acc_l;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) acc_l[e] = 0.0f;
-  bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)(l32 == 0 ? 1.0f : 0.0f);
-#endif
 
   const int n_tiles = (rows + BKV - 1) / BKV;
   // Phase 2t is group 0's matrix step t and phase 2t+1 its softmax of tile
@@ -229,9 +214,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const uint16_t* _
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc_o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s][i], pf[s], acc_o[i], 0, 0, 0);
-#if MOSS_ATTN_MSUM
-      acc_l = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[s], acc_l, 0, 0, 0);
-#endif
     }
   };
   auto softmax = [&](int t) {
@@ -255,11 +237,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const uint16_t* _
     if (__builtin_amdgcn_ballot_w64(mloc > m_use + kLazy) != 0ull) {
       const float m_new = fmaxf(m_use, mloc);
       const float corr = __builtin_amdgcn_exp2f(m_use - m_new);
-#if MOSS_ATTN_MSUM
-      acc_l[0] *= corr;
-#else
       l_run *= corr;
-#endif
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -267,9 +245,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const uint16_t* _
       m_use = m_new;
     }
     const float moff = (m_use == -INFINITY) ? 0.0f : m_use;
-#if !MOSS_ATTN_MSUM
     float lsum = 0.0f;
-#endif
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -277,14 +253,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const uint16_t* _
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) {
           const float p = __builtin_amdgcn_exp2f(fmaf(sacc[h2][8 * half + tt], scale_log2, -moff));
-#if !MOSS_ATTN_MSUM
           lsum += p;
-#endif
           pf[2 * h2 + half][tt] = (__bf16)p;
         }
-#if !MOSS_ATTN_MSUM
     l_run += pair_sum(lsum);
-#endif
   };
   // ends of the even phases: nothing is scheduled across them
   auto bar = [&]() { __builtin_amdgcn_sched_barrier(0); };
@@ -344,9 +316,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const uint16_t* _
     pv(n_tiles - 1);
   }
 
-#if MOSS_ATTN_MSUM
-  l_run = pair_sum(acc_l[0]);
-#endif
   // acc_o[i][4q + e] = O^T[dim = 32 i + 8 q + 4 hh + e][query l32]
   if (qrow < rows) {
     const float inv = 1.0f / l_run;
