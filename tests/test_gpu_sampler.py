@@ -116,3 +116,21 @@ def test_stack_skip_every_block_passes_rows_through():
     np.testing.assert_array_equal(got[1, :n], acts["txt"][1, :n])
     assert np.all(got[1, n:geom.n_txt] == 0)
     np.testing.assert_array_equal(got[1, geom.n_txt:], acts["x"][1])
+
+
+def test_stack_skip_35_blocks():
+    """35 blocks (the modulations of a call go to the GPU in launches of at most 32 weight matrices,
+    so the skip table of the 33rd-35th blocks rides in a second launch): blocks 3 and 33 skipped for
+    item 0, block 34 for item 1."""
+    geom = synth.smaller(synth.CONFIGS["c0"], batch=2, txt_len=(8, 2))
+    n = 35
+    G.say(f"stack_skip c0 x{n}")
+    acts = synth.make_activations(geom, 15)
+    ws = [synth.make_block_weights(geom, 15, i) for i in range(n)]
+    skip = [[i in (3, 33), i == 34] for i in range(n)]
+    got = G.host_f64(_stack_skip_gpu(geom, acts, ws, skip))
+    cos, sin = ob.rope_tables(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, geom.head_dim)
+    x, txt, cond = ob.widen_bf16(acts["x"]), ob.widen_bf16(acts["txt"]), ob.widen_bf16(acts["cond"])
+    ref = osm.stack_forward_skip(x, txt, acts["txt_len"], cond, [ob.weights_f64(w) for w in ws], skip, cos, sin,
+                                 geom.eps)
+    check(geom, acts, got, ref)
