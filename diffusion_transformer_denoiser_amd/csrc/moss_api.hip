@@ -297,18 +297,23 @@ int run_stack(const Ctx& c, int n_blocks, const uint16_t* x, const uint16_t* txt
   float* mod = reinterpret_cast<float*>(c.ws + c.L.mod);
   const size_t mod_stride = (size_t)d->batch * 6 * d->d_model;
   {
-    std::vector<const uint16_t*> w_mods(n_blocks);
-    std::vector<unsigned> masks(n_blocks, 0u);
-    for (int i = 0; i < n_blocks; ++i) {
-      w_mods[i] = blocks[i].w_mod;
-      if (skip)
-        for (int b = 0; b < d->batch; ++b)
-          if (skip[(size_t)i * d->batch + b]) masks[i] |= 1u << b;
-    }
     StepTimer t(MOSS_STEP_ADALN, c.st);
-    MOSS_TRY(launch_adaln_gemv_many(reinterpret_cast<const float*>(c.ws + c.L.s_cond), w_mods.data(), masks.data(),
-                                    n_blocks, mod, d->batch, d->d_model, c.st),
-             "adaln_gemv");
+    constexpr int kChunk = 32;  // matrices per launch_adaln_gemv_many call (no host allocation per call)
+    for (int i0 = 0; i0 < n_blocks; i0 += kChunk) {
+      const int k = n_blocks - i0 < kChunk ? n_blocks - i0 : kChunk;
+      const uint16_t* w_mods[kChunk];
+      unsigned masks[kChunk];
+      for (int i = 0; i < k; ++i) {
+        w_mods[i] = blocks[i0 + i].w_mod;
+        masks[i] = 0u;
+        if (skip)
+          for (int b = 0; b < d->batch; ++b)
+            if (skip[(size_t)(i0 + i) * d->batch + b]) masks[i] |= 1u << b;
+      }
+      MOSS_TRY(launch_adaln_gemv_many(reinterpret_cast<const float*>(c.ws + c.L.s_cond), w_mods, masks, k,
+                                      mod + (size_t)i0 * mod_stride, d->batch, d->d_model, c.st),
+               "adaln_gemv");
+    }
   }
   for (int i = 0; i < n_blocks; ++i) {
     const FirstRows rows{x, txt};
