@@ -198,18 +198,22 @@ def traffic_summary(fetch_dir, write_dir, geom):
     print("\n".join(lines))
 
 
-def cpu_baseline(geom, acts, wbits):
-    """Time the float64 oracle on one block forward of the same workload."""
+def cpu_baseline(geom, acts, wbits, min_seconds=10.0, max_forwards=8):
+    """Time the float64 oracle on whole block forwards of the same workload: repeated until about
+    min_seconds of CPU work (at most max_forwards), so the sample is bounded but not one noisy call."""
     from oracle import dit_block as ob
     threads = len(os.sched_getaffinity(0))
     cos, sin = ob.rope_tables(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, geom.head_dim)
     x, txt, cond = ob.widen_bf16(acts["x"]), ob.widen_bf16(acts["txt"]), ob.widen_bf16(acts["cond"])
     w = ob.weights_f64(wbits)
+    n = 0
     t0 = time.perf_counter()
-    ob.block_forward(x, txt, acts["txt_len"], cond, w, cos, sin, geom.eps)
+    while n < max_forwards and (n == 0 or time.perf_counter() - t0 < min_seconds):
+        ob.block_forward(x, txt, acts["txt_len"], cond, w, cos, sin, geom.eps)
+        n += 1
     dt = time.perf_counter() - t0
-    return {"value": 1.0 / dt, "unit": "block-forwards/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full block forward of this workload in float64 NumPy ({dt:.1f} s; BLAS threads = "
+    return {"value": n / dt, "unit": "block-forwards/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} full block forwards of this workload in float64 NumPy ({dt:.1f} s; BLAS threads = "
                       f"{threads} host cores)"}
 
 
