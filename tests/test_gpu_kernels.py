@@ -158,7 +158,8 @@ def test_gemm_column_split_strided():
     assert np.all(got[:, n:] == 0)
 
 
-@pytest.mark.parametrize("m,f,k", [(72, 1024, 256), (1058, 384, 512), (4130, 12288, 3072), (1124, 8192, 256)])
+@pytest.mark.parametrize("m,f,k", [(72, 1024, 256), (1058, 384, 512), (4130, 12288, 3072), (1124, 8192, 256),
+                                   (4300, 12288, 256)])  # 1632 tiles, one workgroup per CU, a part-full last row tile
 def test_gemm_silu(m, f, k):
     """The up projection with the SiLU gate in its epilogue (a9 + a10 as the block runs them)."""
     G.say(f"gemm_silu M={m} F={f} K={k}")
