@@ -175,7 +175,8 @@ def test_gemm_silu(m, f, k):
 
 
 @pytest.mark.parametrize("batch,rows,n,k", [(1, 72, 256, 256), (2, 530, 384, 512), (2, 4130, 3072, 12288),
-                                            (2, 529, 16384, 256)])
+                                            (2, 529, 16384, 256),
+                                            (1, 2048, 16384, 256)])  # 256x256 tiles, two per workgroup
 @pytest.mark.parametrize("to_bf16", [False, True])
 def test_gemm_gated_add(batch, rows, n, k, to_bf16):
     """The out / down projection with the gated residual add in its epilogue (a6 + a7, a11 + a12)."""
