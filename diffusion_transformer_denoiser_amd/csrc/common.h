@@ -95,6 +95,25 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory");
 }
 
+// A raw buffer resource (V#) over `bytes` bytes from `base`: no stride, 32-bit data format
+// (the raw-buffer setting on gfx9-family parts).  Buffer loads past `bytes` return zero.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// As dma16, through a buffer load: 16 bytes per lane from byte offset voff of the buffer rsrc
+// into LDS at lds + 16 lane (buffer_load_dwordx4 ... lds; bounds-checked by the resource).
+__device__ __forceinline__ void dma16_buf(uint32_t voff, u32x4 rsrc, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
 // Per-launch batch metadata passed by value (txt_len lives on the host).
 struct ItemLens {
   int32_t len[MOSS_MAX_BATCH];

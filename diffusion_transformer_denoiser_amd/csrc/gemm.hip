@@ -7,23 +7,21 @@
 // (BM/WM) x (BN/WN) sub-tile whose fp32 accumulators stay in registers for
 // the whole K loop.
 //
-//  * K advances 32 at a time through a ring of LDS stages (five, 160 KiB, for
-//    the 256 x 256 tiles).  Each slab is fetched straight into LDS with
-//    global_load_lds_dwordx4 (issued from asm, see dma16) STAGES - 1 slabs
-//    ahead of its use, so no register staging or LDS store instruction is
-//    needed; five stages rather than four gave the loads one more slab to
-//    land (+0.6% per block).
-//  * The MFMA operands of a slab are read from LDS into registers one k-step
-//    ahead, across the slab boundary: when a wavefront reaches the barrier
-//    that ends slab kt, the fragments of slab kt+1 are already in flight, and
-//    slab kt+2 must be resident.  The barrier is a plain s_barrier after an
-//    explicit vmcnt wait that leaves the newer slabs' loads outstanding.
-//  * A slab row is 64 bytes (32 bf16 of k).  The 16-byte chunk c of row r is
-//    stored at c ^ ((r >> 2) & 3), so the 16 rows a 16-lane group reads for
-//    one operand fragment land in 16 distinct 16-byte slots of the LDS banks.
-//  * Within a k-step the wavefront issues the next k-step's fragment reads
-//    one after each of its first MFMAs (a scheduling-group constraint), so the
-//    reads have most of the step's MFMAs to land.
+//  * K advances 64 at a time through two LDS stages (128 KiB for the 256 x 256
+//    tiles).  Each slab is fetched straight into LDS with buffer_load_dwordx4
+//    ... lds (issued from asm, see dma16_buf), the next slab's loads spread
+//    evenly over the MFMAs of the current slab's first two k16 steps, so they
+//    have the last two steps to land before the slab's one barrier.  A slab
+//    row is 128 bytes: every load covers whole cache lines (32-k slabs read
+//    half lines, twice as many L2 requests; 4096 x 24576 x 3072 went from
+//    519 to 483 us standalone with this scheme).
+//  * The MFMA operands of the next k16 step are read from LDS into registers
+//    during the current one, one read after each of its first MFMAs; nothing
+//    is reordered across those points (sched_barrier), so the reads, loads
+//    and MFMAs issue interleaved in the order written.
+//  * The 16-byte chunk c of row r is stored at c ^ ((r >> 1) & 7), so the 16
+//    rows a 16-lane group reads for one operand fragment land in 16 distinct
+//    16-byte slots of the LDS banks.
 //  * Tiles are numbered in groups of six column tiles, row-major within a
 //    group, and workgroup ids (dealt round-robin over the 8 XCDs) are
 //    remapped so each XCD runs a contiguous stretch of that order: the ~32
@@ -35,8 +33,8 @@
 //    results leave in 16-byte stores (half the store instructions of 8-byte
 //    ones: QKV 271 -> 257 us, up 589 -> 583 us on one box).
 //  * Launches with more tiles than CUs run one workgroup per CU, each taking
-//    every G-th tile in turn; its slab ring runs on across its tiles, so a
-//    tile's first slabs are in LDS when the previous tile's epilogue ends.
+//    every G-th tile in turn; its loads run on across its tiles, so a tile's
+//    first slab is in LDS when the previous tile's epilogue starts.
 // There is no split-K and no atomic: results are identical call to call.
 //
 // Epilogues (the MOSS-Image transformer page's SiLU and gated-add kernels,
@@ -57,7 +55,7 @@
 
 namespace {
 
-constexpr int KB = 32;      // k per slab
+constexpr int KB = 64;      // k per slab (a 128-byte row segment: whole cache lines)
 
 enum Epi { kStore = 0, kSiluGate = 1, kGatedAdd = 2, kQkvPack = 3 };
 
@@ -80,14 +78,7 @@ struct EpiArgs {
   int col0;           // kQkvPack: absolute column of this launch's column 0
 };
 
-#ifndef MOSS_GEMM_GROUP
-#define MOSS_GEMM_GROUP 6
-#endif
-constexpr int kGroupN = MOSS_GEMM_GROUP;
-// LDS fragment reads placed after each MFMA of the other k-step (0: the compiler's own order)
-#ifndef MOSS_GEMM_SCHED
-#define MOSS_GEMM_SCHED 1
-#endif  // column tiles per group
+constexpr int kGroupN = 6;  // column tiles per group of the tile order
 
 // Workgroup id -> (tile_m, tile_n).  Logical order: column tiles in groups of
 // kGroupN, each group row-major (N fastest); workgroup ids are dealt
@@ -102,38 +93,6 @@ __device__ __forceinline__ void tile_of(int id, int mt, int nt, int& tm, int& tn
   const int cols = min(kGroupN, nt - g * kGroupN);
   tm = r / cols;
   tn = g * kGroupN + r % cols;
-}
-
-// Wait until at most `ahead` slabs of loads (PER instructions each, the
-// newest ones) are still in flight, then barrier.  vmcnt takes an immediate,
-// so each count from MAXA down has its own instruction.
-template <int PER, int MAXA>
-__device__ __forceinline__ void wait_slabs_barrier(int ahead) {
-  if constexpr (MAXA >= 1) {
-    if (ahead >= MAXA) {
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(MAXA * PER) : "memory");
-      return;
-    }
-    wait_slabs_barrier<PER, MAXA - 1>(ahead);
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  }
-}
-
-// Instruction order for one k-step: one MFMA, then RPM LDS reads, repeated
-// until the NR reads are placed, then the remaining MFMAs, so the last read
-// still has several MFMAs behind it before its data are needed.
-template <int RPM, int NR, int NMFMA>
-__device__ __forceinline__ void sched_interleave() {
-  if constexpr (NR > 0 && NMFMA > 0) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, NR < RPM ? NR : RPM, 0);
-    sched_interleave<RPM, (NR > RPM ? NR - RPM : 0), NMFMA - 1>();
-  } else if constexpr (NR > 0) {
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-  } else if constexpr (NMFMA > 0) {
-    __builtin_amdgcn_sched_group_barrier(0x008, NMFMA, 0);
-  }
 }
 
 // acc[i][j] is a 32 x 32 tile of c^T: lane holds row m = l32 of c and
@@ -228,7 +187,7 @@ __device__ __forceinline__ void epilogue_gated_lds(const f32x16 (&acc)[BN / WN /
   constexpr int FM = BM / 32;
   constexpr int LDR = 132;  // floats per staged row
   static_assert(WM == 1 && WN == 8 && BN == 256, "one wavefront row of 32-column strips");
-  static_assert(BM * LDR * 4 <= 160 * 1024, "half a tile fits the LDS");
+  static_assert(BM * LDR * 4 <= 2 * (BM + BN) * KB * 2, "half a tile fits the two stages");
   float* st = reinterpret_cast<float*>(smem);
   const int lane = threadIdx.x & 63;
   const int c4 = 4 * (lane & 31);  // this lane's 4 columns of the half
@@ -399,7 +358,7 @@ __device__ __forceinline__ void epilogue_qkv(const f32x16 (&acc)[BN / WN / 32][B
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int STAGES = 4>
+template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __restrict__ a, int lda,
                                                              const uint16_t* __restrict__ w, int ldw,
                                                              uint16_t* __restrict__ c, int ldc, int m_begin,
@@ -407,21 +366,20 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int AB = BM * KB * 2, BB = BN * KB * 2;          // bytes per slab
+  constexpr int NR = FM + FN, NMF = FM * FN;             // fragment reads and MFMAs per k-step
+  constexpr int AB = BM * KB * 2, BB = BN * KB * 2, SB = AB + BB;  // bytes per slab (one stage)
   // 1 KiB load instructions per wavefront; when the A chunks do not divide among the wavefronts
-  // (224-row tiles: 14 chunks), the last wavefronts load the last chunk again (same bytes, same place)
+  // (224-row tiles: 28 chunks), the last wavefronts load the last chunk again (same bytes, same place)
   constexpr int CA = AB / 1024, CB = BB / 1024;
   constexpr int LA = (CA + NW - 1) / NW, LB = CB / NW;
   constexpr int PER = LA + LB;
   static_assert(CA * 1024 == AB && LB * NW * 1024 == BB, "slab / wavefront mismatch");
-  static_assert(STAGES >= 4 && (STAGES - 3) * PER <= 63, "ring depth / vmcnt range");
   static_assert(EPI != kSiluGate || FN % 2 == 0, "the SiLU epilogue pairs gate and up fragments per wavefront");
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * (AB + BB)];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * SB];
 
   // This launch covers rows [m_begin, m).  Workgroup b computes tiles b, b + G, b + 2G, ... of the
-  // launch (G workgroups); the slab ring runs on from one of its tiles into the next, so the next
-  // tile's first slabs load while this one finishes, and its epilogue's stores drain during the
-  // next tile's first k-steps.
+  // launch (G workgroups); the loads run on from one of its tiles into the next, so a tile's first
+  // slab is in LDS when the previous tile's epilogue starts.
   const int mt = (m - m_begin + BM - 1) / BM, ntn = n / BN, ntiles = mt * ntn;
   const int G = gridDim.x;
   const int mine = (ntiles - (int)blockIdx.x + G - 1) / G;
@@ -429,27 +387,29 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
   const int wm = wave / WN, wn = wave % WN;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  // the operands as buffers (the launcher checks that both fit 32-bit byte offsets)
+  const u32x4 ra = buffer_rsrc(a, (uint32_t)((size_t)m * lda * 2));
+  const u32x4 rw = buffer_rsrc(w, (uint32_t)((size_t)n * ldw * 2));
 
   // Load instruction i of wavefront `wave` fills the 1 KiB at (wave + NW*i) of a slab: rows
-  // 16*(wave + NW*i) + lane/4, stored slot lane%4, which holds chunk (lane%4) ^ ((row >> 2) & 3).
+  // 8*(wave + NW*i) + lane/8, stored slot lane%8, which holds chunk (lane%8) ^ ((row >> 1) & 7).
   // Rows past m are clamped to m - 1; their results are never stored.
   uint32_t ca[LA];  // LDS byte offset of A chunk i of this wavefront
 #pragma unroll
   for (int i = 0; i < LA; ++i) ca[i] = 1024u * min(wv + NW * i, CA - 1);
-  const uint16_t* ga[LA];
-  const uint16_t* gb[LB];
-  auto aim = [&](int r) {  // point the loads at this workgroup's tile r
+  uint32_t va[LA], vb[LB];  // byte offsets of this lane's 16 bytes of slab 0 of the current tile
+  auto aim = [&](int r) {    // point the loads at this workgroup's tile r
     int tm, tn;
     tile_of(blockIdx.x + r * G, mt, ntn, tm, tn);
     const int m0 = m_begin + tm * BM, n0 = tn * BN;
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-      const int rr = min(wv + NW * i, CA - 1) * 16 + (lane >> 2);
-      ga[i] = a + (size_t)min(m0 + rr, m - 1) * lda + ((lane & 3) ^ ((rr >> 2) & 3)) * 8;
+      const int rr = min(wv + NW * i, CA - 1) * 8 + (lane >> 3);
+      va[i] = (uint32_t)(((size_t)min(m0 + rr, m - 1) * lda + ((lane & 7) ^ ((rr >> 1) & 7)) * 8) * 2);
     }
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
-      const int rr = (wave + NW * i) * 16 + (lane >> 2);
+      const int rr = (wave + NW * i) * 8 + (lane >> 3);
       int wrow = n0 + rr;
       if (EPI == kSiluGate) {
         // tile row rr -> wavefront rr / TN, fragment f = (rr % TN) / 32: even f = gate rows, odd f =
@@ -458,59 +418,60 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
         const int zc = tn * (BN / 2) + (rr / TN) * (TN / 2) + (f / 2) * 32 + (rr & 31);
         wrow = ((f & 1) ? n / 2 : 0) + zc;
       }
-      gb[i] = w + (size_t)wrow * ldw + ((lane & 3) ^ ((rr >> 2) & 3)) * 8;
+      vb[i] = (uint32_t)(((size_t)wrow * ldw + ((lane & 7) ^ ((rr >> 1) & 7)) * 8) * 2);
     }
   };
   const uint32_t lds0 = (uint32_t)(uintptr_t)(MOSS_LDS char*)smem;
-  int lt = 0, lk = 0, lst = 0;  // the next load: tile, slab within it, ring stage
-  auto issue = [&]() {
-    const uint32_t base = lds0 + (uint32_t)(lst * (AB + BB));
-#pragma unroll
-    for (int i = 0; i < LA; ++i) dma16(ga[i] + lk * KB, base + ca[i]);
-#pragma unroll
-    for (int i = 0; i < LB; ++i) dma16(gb[i] + lk * KB, base + AB + 1024u * (wv + NW * i));
-    if (++lst == STAGES) lst = 0;
-    if (++lk == nk) {
-      lk = 0;
-      if (++lt < mine) aim(lt);
+  int lt = 0, lk = 0, lst = 0;  // the next slab to load: tile, slab within it, stage
+  auto issue_one = [&](int q) {  // load instruction q of that slab; the last one moves on
+    const uint32_t base = lds0 + (uint32_t)(lst * SB);
+    if (q < LA)
+      dma16_buf(va[q] + lk * (KB * 2), ra, base + ca[q]);
+    else
+      dma16_buf(vb[q - LA] + lk * (KB * 2), rw, base + AB + 1024u * (wv + NW * (q - LA)));
+    if (q == PER - 1) {
+      lst ^= 1;
+      if (++lk == nk) {
+        lk = 0;
+        if (++lt < mine) aim(lt);
+      }
     }
   };
-  // byte offsets of this lane's fragments within a stage, for the two k16 steps of a slab
-  int offa[2][FM], offb[2][FN];
+  // byte offsets of this lane's fragments within a stage, for the four k16 steps of a slab
+  int offa[4][FM], offb[4][FN];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < 4; ++s) {
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       const int r = wm * TM + j * 32 + l32;
-      offa[s][j] = r * 64 + ((2 * s + hh) ^ ((r >> 2) & 3)) * 16;
+      offa[s][j] = r * (KB * 2) + ((2 * s + hh) ^ ((r >> 1) & 7)) * 16;
     }
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
       const int r = wn * TN + i * 32 + l32;
-      offb[s][i] = AB + r * 64 + ((2 * s + hh) ^ ((r >> 2) & 3)) * 16;
+      offb[s][i] = AB + r * (KB * 2) + ((2 * s + hh) ^ ((r >> 1) & 7)) * 16;
     }
   }
-  // reads in the order the k-step's MFMAs first use them (w0 a0 w1 a1 a2 a3 ...; the MFMAs run
-  // over the activation fragments in the outer loop), so the first MFMAs' operands arrive first
-  auto ldfrag = [&](int stage, int s, bf16x8* fa, bf16x8* fw) {
-    const char* base = smem + stage * (AB + BB);
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      if (j < FN) fw[j] = *reinterpret_cast<const bf16x8*>(base + offb[s][j]);
-      fa[j] = *reinterpret_cast<const bf16x8*>(base + offa[s][j]);
-    }
-#pragma unroll
-    for (int i = FM; i < FN; ++i) fw[i] = *reinterpret_cast<const bf16x8*>(base + offb[s][i]);
+  // fragment read x of a k-step, in the order the step's MFMAs first use them (w0 a0 w1 .. a1 ..;
+  // the MFMAs run over the weight fragments in the inner loop)
+  auto rd = [&](const char* st, int s, int x, bf16x8* fa, bf16x8* fw) {
+    if (x == 0)
+      fw[0] = *reinterpret_cast<const bf16x8*>(st + offb[s][0]);
+    else if (x == 1)
+      fa[0] = *reinterpret_cast<const bf16x8*>(st + offa[s][0]);
+    else if (x < FN + 1)
+      fw[x - 1] = *reinterpret_cast<const bf16x8*>(st + offb[s][x - 1]);
+    else
+      fa[x - FN] = *reinterpret_cast<const bf16x8*>(st + offa[s][x - FN]);
   };
 
   aim(0);
+  if (total > 0)
 #pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p)
-    if (p < total) issue();
-  // slabs 0 and 1 resident before the loop (iteration 0 prefetches slab 1)
-  wait_slabs_barrier<PER, STAGES - 3>(min(total, STAGES - 1) - 2);
+    for (int q = 0; q < PER; ++q) issue_one(q);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
-  int g = 0, cs = 0;  // the slab being consumed (counted over this workgroup's tiles) and its stage
+  int g = 0;  // the slab being consumed, counted over this workgroup's tiles
   for (int r = 0; r < mine; ++r) {
     int tm, tn;
     tile_of(blockIdx.x + r * G, mt, ntn, tm, tn);
@@ -524,38 +485,42 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    bf16x8 fa0[FM], fw0[FN], fa1[FM], fw1[FN];
-    ldfrag(cs, 0, fa0, fw0);
     for (int kt = 0; kt < nk; ++kt, ++g) {
-      // the stage of slab g-1, whose last reads finished before the previous barrier
-      if (g + STAGES - 1 < total) issue();
-      const int cn = cs + 1 == STAGES ? 0 : cs + 1;
-      ldfrag(cs, 1, fa1, fw1);
+      const char* cur = smem + (g & 1) * SB;
+      const bool more = g + 1 < total;  // slab g + 1 is loaded into the other stage during steps 0-1
+      bf16x8 fa[2][FM], fw[2][FN];
 #pragma unroll
-      for (int j = 0; j < FM; ++j)
+      for (int x = 0; x < NR; ++x) rd(cur, 0, x, fa[0], fw[0]);
+#pragma clang loop unroll(full)
+      for (int s = 0; s < 4; ++s) {
+#pragma clang loop unroll(full)
+        for (int t = 0; t < NMF; ++t) {
+          const int j = t / FN, i = t % FN;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[s & 1][i], fa[s & 1][j], acc[i][j], 0, 0, 0);
+          // one fragment read of the next k-step after each of the first MFMAs (the rest after the
+          // last one when there are more reads than MFMAs), and the next slab's loads spread evenly
+          // over the MFMAs of k-steps 0 and 1; nothing moves across these points
+          __builtin_amdgcn_sched_barrier(0);
+          if (s < 3) {
 #pragma unroll
-        for (int i = 0; i < FN; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw0[i], fa0[j], acc[i][j], 0, 0, 0);
-      // slab g+1 is resident; a tile's last k-step re-reads its own stage so the wait counts stay exact
-      ldfrag(kt + 1 < nk ? cn : cs, 0, fa0, fw0);
+            for (int x = t; x < (t + 1 == NMF ? NR : t + 1); ++x)
+              if (x < NR) rd(cur, s + 1, x, fa[(s + 1) & 1], fw[(s + 1) & 1]);
+          }
+          if (s < 2 && more) {
+            const int u = s * NMF + t;
 #pragma unroll
-      for (int j = 0; j < FM; ++j)
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw1[i], fa1[j], acc[i][j], 0, 0, 0);
-#if MOSS_GEMM_SCHED
-      // issue each k-step's fragment reads early in the other k-step's MFMAs
-      sched_interleave<MOSS_GEMM_SCHED, FM + FN, FM * FN>();
-      sched_interleave<MOSS_GEMM_SCHED, FM + FN, FM * FN>();
-#endif
-      // slab g+2 resident for the next k-step (the slabs issued after it may stay in flight)
-      wait_slabs_barrier<PER, STAGES - 3>(min(total - 1, g + STAGES - 1) - (g + 2));
-      cs = cn;
+            for (int q = u * PER / (2 * NMF); q < (u + 1) * PER / (2 * NMF); ++q) issue_one(q);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // slab g + 1 resident and every read of slab g done before the next slab's loads overwrite it
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     }
 
     if constexpr (EPI == kQkvPack) {
-      // the stage of the tile's last slab stays free until the next tile's first k-step
-      char* spare = smem + (cs == 0 ? STAGES - 1 : cs - 1) * (AB + BB);
+      // the stage of the tile's last slab stays free until the next tile's second slab is loaded
+      char* spare = smem + ((g + 1) & 1) * SB;
       epilogue_qkv<BM, BN, WM, WN>(acc, spare, m0, n0, wave, wm, wn, l32, hh, m, ep);
     } else if constexpr (EPI == kGatedAdd && WM == 1 && WN == 8 && BN == 256) {
       if (r + 1 == mine)
@@ -589,6 +554,9 @@ int cu_count() {
 template <int EPI>
 hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_t* w, int ldw, uint16_t* c, int ldc,
                   const EpiArgs& ep, hipStream_t st) {
+  // the kernels address both operands through 32-bit buffer byte offsets
+  if ((size_t)m * lda * 2 > 0xffffffffu || (size_t)n * ldw * 2 > 0xffffffffu || k % KB != 0)
+    return hipErrorInvalidValue;
   if (n % 256 == 0) {
     const int nt = n / 256, full = m / 256, rem = m % 256, cus = cu_count();
     bool split = false;
@@ -606,7 +574,7 @@ hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_
       const int mt = (m + 255) / 256, rounds = mt * nt / cus, left = mt * nt % cus;
       const int nt1 = rounds * cus / mt, nt2 = nt - nt1, mt2 = (m + 127) / 128;
       if (rounds >= 1 && left > 0 && 2 * left <= cus && nt1 > 0 && nt2 > 0 && mt2 * nt2 <= cus) {
-        hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI, 5>), dim3(std::min(mt * nt1, cus)), dim3(512), 0, st, a,
+        hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI>), dim3(std::min(mt * nt1, cus)), dim3(512), 0, st, a,
                            lda, w, ldw, c, ldc, 0, m, nt1 * 256, k, ep);
         EpiArgs ep2 = ep;
         ep2.col0 = ep.col0 + nt1 * 256;
@@ -625,13 +593,13 @@ hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_
       // 224 x 64 (1 per SIMD) kept less.
       const int t256 = ((m + 255) / 256) * nt, t224 = ((m + 223) / 224) * nt;
       if (!split && (t224 + cus - 1) / cus == (t256 + cus - 1) / cus) {
-        hipLaunchKernelGGL((gemm_nt_kernel<224, 256, 1, 8, EPI, 5>), dim3(t224), dim3(512), 0, st, a, lda, w, ldw, c,
+        hipLaunchKernelGGL((gemm_nt_kernel<224, 256, 1, 8, EPI>), dim3(t224), dim3(512), 0, st, a, lda, w, ldw, c,
                            ldc, 0, m, n, k, ep);
         return hipGetLastError();
       }
     }
     // one workgroup per CU, each taking every cus-th tile
-    hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI, 5>), dim3(std::min(((m_main + 255) / 256) * nt, cus)),
+    hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI>), dim3(std::min(((m_main + 255) / 256) * nt, cus)),
                        dim3(512), 0, st, a, lda, w, ldw, c, ldc, 0, m_main, n, k, ep);
     if (split) {
       // 64 x 128 tiles: twice the workgroups of 64 x 256 ones, so twice the CUs stream the weight
