@@ -247,7 +247,8 @@ def block_residual(h0, cond, txt_len, n_txt: int, w: dict, cos, sin, eps: float,
     mods = r32(adaln_modulation(cond, w["w_mod"]))  # [B, 6D]
     valid = key_mask(n_txt, t - n_txt, txt_len)
     out = np.empty_like(h0)
-    steps = {k: [] for k in ("mod", "a", "qkv", "q", "k", "v", "attn", "o2", "h1", "m", "u", "z", "y")}
+    steps = {k: [] for k in ("mod", "cos", "sin", "a", "qkv", "q", "k", "v", "attn", "o2", "h1", "m", "u", "z",
+                             "y")}
     for b in range(bsz):
         mb = split_modulation(mods[b], d)
         a = r16(modulated_rmsnorm(h0[b], mb["shift1"], mb["scale1"], eps))
@@ -265,7 +266,8 @@ def block_residual(h0, cond, txt_len, n_txt: int, w: dict, cos, sin, eps: float,
         y = z @ w["w_down"].T
         out[b] = gated_add(h1, mb["gate2"], y)
         if keep:
-            for name, val in (("mod", mods[b]), ("a", a), ("qkv", qkv), ("q", q), ("k", k), ("v", v),
+            for name, val in (("mod", mods[b]), ("cos", cos), ("sin", sin), ("a", a), ("qkv", qkv), ("q", q),
+                              ("k", k), ("v", v),
                               ("attn", o), ("o2", o2), ("h1", h1), ("m", m), ("u", u), ("z", z), ("y", y)):
                 steps[name].append(val)
     if keep:

@@ -78,6 +78,40 @@ def pin_brute_force_tiny():
         _close(got, ref)
 
 
+STEP_NAMES = ("mod", "cos", "sin", "a", "qkv", "q", "k", "attn", "o2", "h1", "m", "u", "z", "y")
+
+
+def _brute_rounded(geom, x, txt, txt_len, cond, w):
+    """The brute force's rounding-point mode: (output, {step: [B, ...] array})."""
+    ang = bf.angles(bf.positions(geom.n_txt, geom.grid_h, geom.grid_w), geom.theta, geom.head_dim)
+    wl = {k: v.tolist() for k, v in w.items()}
+    steps = {}
+    out = bf.block(x.tolist(), txt.tolist(), [int(n) for n in txt_len], cond.tolist(), wl, ang, geom.eps,
+                   rounded=True, steps=steps)
+    return np.array(out), {k: np.array(v) for k, v in steps.items()}
+
+
+def pin_rounded_mode_brute_tiny():
+    """The oracle's rounding-point mode == the brute force's, step by step, on tiny geometries.
+
+    The twin rounds on its own (bf16 on the float64 bits, float32 through
+    struct), so a rounding point dropped, added or moved on either side shows
+    in the step where it happens: the float32 modulation and rotary tables, the
+    bf16 norm outputs, qkv, q and k, softmax weights, attention output and z,
+    and the unrounded residual and projection sums."""
+    for geom in tiny_geoms():
+        x, txt, lens, cond, ws = f64_inputs(geom, seed=6, garbage_pad=True)
+        cos, sin = ob.rope_tables(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, geom.head_dim)
+        got, st = ob.block_forward(x, txt, lens, cond, ws[0], cos, sin, geom.eps, rounded=True, keep=True)
+        ref, rst = _brute_rounded(geom, x, txt, lens, cond, ws[0])
+        for name in STEP_NAMES:
+            try:
+                _close(st[name], rst[name], 1e-12)
+            except AssertionError as exc:
+                raise AssertionError(f"{geom.name} step {name}: {exc}") from None
+        _close(got, ref, 1e-12)
+
+
 def pin_brute_force_stack():
     """A 2-block oracle stack == the brute-force block applied twice."""
     geom = tiny_geoms()[1]
@@ -458,6 +492,43 @@ def pin_denoiser_brute_tiny():
         _close(got, np.array(ref), 1e-11)
 
 
+def _brute_denoiser(geom, lat, enc, lens, t, ends, ws, skip=None, rounded=False):
+    ang = bf.angles(bf.positions(geom.n_txt, geom.grid_h, geom.grid_w), geom.theta, geom.head_dim)
+    return np.array(bf.denoiser(lat.tolist(), enc.tolist(), [int(n) for n in lens], [float(v) for v in t],
+                                {k: v.tolist() for k, v in ends.items()},
+                                [{k: v.tolist() for k, v in w.items()} for w in ws], ang, geom.eps, skip=skip,
+                                rounded=rounded))
+
+
+def pin_denoiser_skip_brute():
+    """A per-(block, item) skip table: the forward == the loop-only twin told to skip the same
+    blocks for the same items (the guidance pass's skipped block, the CUDA port page, PR #2281,
+    "What this changes"); every pattern of a 2-item, 2-block stack, plus the item that skips
+    everything, whose velocity is the final norm of its latent rows alone."""
+    geom = tiny_geoms()[1]
+    lat, enc, lens, t, ends, ws = _denoiser_case(geom, 9, n_blocks=2, std=0.2)
+    cos, sin = ob.rope_tables(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, geom.head_dim)
+    for skip in ([[False, True], [False, False]], [[True, False], [False, True]], [[False, False], [True, True]],
+                 [[True, True], [True, True]]):
+        got = od.denoiser_forward(lat, enc, lens, t, ends, ws, cos, sin, geom.eps, skip=skip)
+        _close(got, _brute_denoiser(geom, lat, enc, lens, t, ends, ws, skip=skip), 1e-11)
+    skip = [[False, True], [False, True]]
+    got = od.denoiser_forward(lat, enc, lens, t, ends, ws, cos, sin, geom.eps, skip=skip)
+    cond = od.timestep_cond(t, ends["w_t1"], ends["w_t2"])
+    alone = od.final_velocity((lat @ ends["w_in"].T)[1:2], cond[1:2], ends["w_fmod"], ends["w_final"], geom.eps)
+    _close(got[1:2], alone, 1e-12)
+
+
+def pin_denoiser_rounded_brute():
+    """The forward's rounding-point mode == the twin's (its own rounding), with a skipped block."""
+    geom = tiny_geoms()[1]
+    lat, enc, lens, t, ends, ws = _denoiser_case(geom, 10, n_blocks=2, std=0.2)
+    cos, sin = ob.rope_tables(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, geom.head_dim)
+    skip = [[False, False], [True, False]]
+    got = od.denoiser_forward(lat, enc, lens, t, ends, ws, cos, sin, geom.eps, rounded=True, skip=skip)
+    _close(got, _brute_denoiser(geom, lat, enc, lens, t, ends, ws, skip=skip, rounded=True), 1e-12)
+
+
 def pin_denoiser_identity_stack():
     """With every gate zero the stack is the identity: the velocity is the final
     norm of the latent rows alone, whatever the prompt; and the final norm is
@@ -482,6 +553,7 @@ def pin_denoiser_identity_stack():
 
 ALL_PINS = [
     pin_brute_force_tiny,
+    pin_rounded_mode_brute_tiny,
     pin_brute_force_stack,
     pin_torch_attention,
     pin_torch_rmsnorm,
@@ -504,8 +576,20 @@ ALL_PINS = [
     pin_skip_block,
     pin_timestep_features,
     pin_denoiser_brute_tiny,
+    pin_denoiser_skip_brute,
+    pin_denoiser_rounded_brute,
     pin_denoiser_identity_stack,
 ]
+
+
+def first_failing_pin():
+    """The name of the first pin that fails (or raises) on the oracle as it stands, or None."""
+    for p in ALL_PINS:
+        try:
+            p()
+        except Exception:  # noqa: BLE001 - any exception counts as a failed pin
+            return p.__name__
+    return None
 
 
 def failing_pins():

@@ -6,6 +6,9 @@ the pages' planted controls that "drop or add one rounding point" and must
 come out red (MOSS-Image encoder page, PR #1512, "Receipt").  The mistakes are
 planted in the oracle, on the CPU; nothing here touches the GPU library.
 """
+import inspect
+import textwrap
+
 import numpy as np
 import pytest
 
@@ -193,14 +196,14 @@ def test_unmutated_oracle_passes_every_pin():
 def test_mutant_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
     monkeypatch.setattr(ob, attr, fn)
-    assert P.failing_pins(), f"planted mistake {name!r} passed every pin"
+    assert P.first_failing_pin(), f"planted mistake {name!r} passed every pin"
 
 
 @pytest.mark.parametrize("name", sorted(SAMPLER_MUTANTS))
 def test_sampler_mutant_is_caught(name, monkeypatch):
     attr, fn = SAMPLER_MUTANTS[name]
     monkeypatch.setattr(osm, attr, fn)
-    assert P.failing_pins(), f"planted mistake {name!r} passed every pin"
+    assert P.first_failing_pin(), f"planted mistake {name!r} passed every pin"
 
 
 _orig_den = {name: getattr(od, name) for name in ("timestep_features", "timestep_cond", "final_velocity")}
@@ -248,4 +251,84 @@ DENOISER_MUTANTS = {
 def test_denoiser_mutant_is_caught(name, monkeypatch):
     attr, fn = DENOISER_MUTANTS[name]
     monkeypatch.setattr(od, attr, fn)
-    assert P.failing_pins(), f"planted mistake {name!r} passed every pin"
+    assert P.first_failing_pin(), f"planted mistake {name!r} passed every pin"
+
+
+# ---- the rounding-point mode ----------------------------------------------------------------
+# The pages' planted controls "drop or add one rounding point" (encoder page, PR #1512,
+# "Receipt"); here each control is the oracle's block with one rounding point of its
+# rounded mode taken out, or one added where the GPU path keeps a value unrounded.
+
+_BLOCK_SRC = textwrap.dedent(inspect.getsource(ob.block_residual))
+
+ROUNDING_MUTANTS = {
+    # dropped
+    "drop_mod_f32": ('mods = r32(adaln_modulation(cond, w["w_mod"]))', 'mods = adaln_modulation(cond, w["w_mod"])'),
+    "drop_rope_f32": ("cos, sin = round_f32(cos), round_f32(sin)", "cos, sin = cos, sin"),
+    "drop_a": ('a = r16(modulated_rmsnorm(h0[b], mb["shift1"], mb["scale1"], eps))',
+               'a = modulated_rmsnorm(h0[b], mb["shift1"], mb["scale1"], eps)'),
+    "drop_qkv": ('qkv = r16(a @ w["w_qkv"].T)', 'qkv = a @ w["w_qkv"].T'),
+    "drop_qk": ('w["q_gain"], w["k_gain"], cos, sin, eps, r16)', 'w["q_gain"], w["k_gain"], cos, sin, eps, _ident)'),
+    "drop_p": ("attention(q, k, v, valid[b], r16)", "attention(q, k, v, valid[b], _ident)"),
+    "drop_attn_out": ("o = r16(attention(q, k, v, valid[b], r16))", "o = attention(q, k, v, valid[b], r16)"),
+    "drop_m": ('m = r16(modulated_rmsnorm(h1, mb["shift2"], mb["scale2"], eps))',
+               'm = modulated_rmsnorm(h1, mb["shift2"], mb["scale2"], eps)'),
+    "drop_z": ("z = r16(silu_gate(u, f))", "z = silu_gate(u, f)"),
+    # added
+    "add_o2": ('o2 = o @ w["w_out"].T', 'o2 = r16(o @ w["w_out"].T)'),
+    "add_h1": ('h1 = gated_add(h0[b], mb["gate1"], o2)', 'h1 = r16(gated_add(h0[b], mb["gate1"], o2))'),
+    "add_u": ('u = m @ w["w_up"].T', 'u = r16(m @ w["w_up"].T)'),
+    "add_y": ('y = z @ w["w_down"].T', 'y = r16(z @ w["w_down"].T)'),
+    "add_out": ('out[b] = gated_add(h1, mb["gate2"], y)', 'out[b] = r16(gated_add(h1, mb["gate2"], y))'),
+}
+
+
+def _mutated_block(old, new):
+    assert _BLOCK_SRC.count(old) == 1, f"the control's text must occur once in block_residual: {old!r}"
+    ns = dict(vars(ob))
+    exec(compile(_BLOCK_SRC.replace(old, new), "<planted control>", "exec"), ns)  # noqa: S102
+    return ns["block_residual"]
+
+
+@pytest.mark.parametrize("name", sorted(ROUNDING_MUTANTS))
+def test_rounding_point_control_is_caught(name, monkeypatch):
+    monkeypatch.setattr(ob, "block_residual", _mutated_block(*ROUNDING_MUTANTS[name]))
+    assert P.first_failing_pin(), f"planted control {name!r} passed every pin"
+
+
+def _qk_unrounded(q, k, qg, kg, cos, sin, eps, rnd=lambda a: a):
+    return _orig["qk_norm_rope"](q, k, qg, kg, cos, sin, eps)
+
+
+def test_qk_left_unrounded_is_caught(monkeypatch):
+    """q and k not stored in bf16 in the rounded mode (the q/k kernel's own rounding point)."""
+    monkeypatch.setattr(ob, "qk_norm_rope", _qk_unrounded)
+    assert P.first_failing_pin(), "q/k left unrounded passed every pin"
+
+
+def test_denoiser_skip_other_item_is_caught(monkeypatch):
+    """The skip table applied to the other item of the guidance pair."""
+    orig = od.denoiser_forward
+
+    def flipped(*args, skip=None, **kw):
+        return orig(*args, skip=[list(reversed(r)) for r in skip] if skip is not None else None, **kw)
+
+    monkeypatch.setattr(od, "denoiser_forward", flipped)
+    assert P.first_failing_pin(), "skip applied to the other item passed every pin"
+
+
+def test_rounding_controls_change_the_rounded_output(monkeypatch):
+    """Each control really changes what the rounded mode computes (so catching it means something):
+    a step of one block, or the output of a 2-block rounded stack (a rounding of the residual
+    between blocks is invisible in one block, whose output is rounded anyway)."""
+    geom = P.tiny_geoms()[1]
+    x, txt, lens, cond, ws = P.f64_inputs(geom, seed=6, n_blocks=2)
+    cos, sin = ob.rope_tables(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, geom.head_dim)
+    _, base = ob.block_forward(x, txt, lens, cond, ws[0], cos, sin, geom.eps, rounded=True, keep=True)
+    stack = ob.stack_forward(x, txt, lens, cond, ws, cos, sin, geom.eps, rounded=True)
+    for name, (old, new) in ROUNDING_MUTANTS.items():
+        monkeypatch.setattr(ob, "block_residual", _mutated_block(old, new))
+        _, st = ob.block_forward(x, txt, lens, cond, ws[0], cos, sin, geom.eps, rounded=True, keep=True)
+        changed = any(not np.array_equal(st[k], base[k]) for k in base)
+        changed |= not np.array_equal(ob.stack_forward(x, txt, lens, cond, ws, cos, sin, geom.eps, rounded=True), stack)
+        assert changed, name
