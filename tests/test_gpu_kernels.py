@@ -10,6 +10,7 @@ import pytest
 from diffusion_transformer_denoiser_amd import moss, synth
 from oracle import dit_block as ob
 
+from . import gates
 from . import gpu_util as G
 
 pytestmark = pytest.mark.gpu
@@ -238,21 +239,13 @@ def test_qk_norm_rope_pack(batch, n_txt, gh, gw, heads):
     assert np.all(qb[:, :, rows:] == 0) and np.all(kb[:, :, rows:] == 0) and np.all(vpad == 0)
 
 
-@pytest.mark.parametrize("batch,n_txt,gh,gw,heads", [
-    (1, 8, 8, 8, 2),      # one 128-row tile of rows, two heads
-    (2, 34, 8, 12, 3),    # items that straddle row tiles; D = 384: a tile spans q and k columns
-    (1, 34, 64, 64, 24),  # the 4096+34-row QKV (column split: the last 6 column tiles run as 128-row tiles)
-])
+@pytest.mark.parametrize("batch,n_txt,gh,gw,heads", gates.QKV_PACK_SHAPES)
 def test_gemm_qkv_pack(batch, n_txt, gh, gw, heads):
     """a3 + a4 fused: the QKV projection with the q/k norm, rotary and packing in its epilogue, against
     the oracle's a4 on the bf16-rounded projection (the value the unfused path stores)."""
-    rows = n_txt + gh * gw
-    d = heads * 128
+    case = gates.qkv_pack_case(batch, n_txt, gh, gw, heads)
+    rows, d, sel = case["rows"], case["d"], case["sel"]
     G.say(f"gemm_qkv_pack B={batch} rows={rows} H={heads}")
-    a = synth.make_tensor(10, 0, (batch * rows, d))
-    w = synth.make_tensor(10, 1, (3 * d, d), std=0.02)
-    gq = synth.normal_bf16(10, (0, 50), (128,), 0.02, offset=1.0)
-    gk = synth.normal_bf16(10, (0, 51), (128,), 0.02, offset=1.0)
     rope = G.empty_f32(2, rows, 64)
     moss.moss_rope_build(n_txt, gh, gw, 10000.0, rope)
     rp = moss.moss_packed_rows(rows)
@@ -262,37 +255,27 @@ def test_gemm_qkv_pack(batch, n_txt, gh, gw, heads):
     for t_ in (q, k, v):
         t_.fill_(0x7FC0)  # NaN pattern: every element must be written
     ws = G.empty_f32(128 * rp)  # the rotary table re-laid for the epilogue: 512 T_pad bytes
-    moss.moss_k_gemm_qkv_pack(batch, rows, heads, 1e-6, G.dev(a), G.dev(w), G.dev(gq), G.dev(gk), rope, q, k, v, ws)
+    moss.moss_k_gemm_qkv_pack(batch, rows, heads, 1e-6, G.dev(case["a"]), G.dev(case["w"]), G.dev(case["gq"]),
+                              G.dev(case["gk"]), rope, q, k, v, ws)
     G.sync()
-    cos, sin = ob.rope_tables(n_txt, gh, gw, 10000.0, 128)
-    # sampled rows at the full size, all rows otherwise
-    sel = np.arange(rows) if rows <= 1100 else np.unique(np.r_[0:40, rows - 40:rows,
-                                                                 np.linspace(0, rows - 1, 120).astype(int)])
     qb, kb = G.host_bits(q), G.host_bits(k)
     vb, vpad = G.unpack_v(G.host_bits(v), rows)
     for b in range(batch):
-        arows = ob.widen_bf16(a.reshape(batch, rows, d)[b][sel])
-        qkv = ob.round_bf16(arows @ ob.widen_bf16(w).T).reshape(len(sel), 3, heads, 128).transpose(1, 2, 0, 3)
-        rq, rk = ob.qk_norm_rope(qkv[0], qkv[1], ob.widen_bf16(gq), ob.widen_bf16(gk), cos[sel], sin[sel], 1e-6)
-        # The projection's fp32 sum can round to the other bf16 neighbour of the exact sum (as the
-        # unfused GEMM's output can); such an input flip moves a normed value by about 2^-8 of the
-        # row scale (about 1), hence the 8e-3 floor; nearly all values must agree to one ulp.
+        rq, rk, rv = gates.qkv_pack_reference(case, b)
         for name, got, ref in ((f"q[{b}]", ob.widen_bf16(qb[b][:, sel]), rq),
                                (f"k[{b}]", ob.widen_bf16(kb[b][:, sel]), rk)):
-            G.assert_ulps(name, got, ref, ulps=2.0, abs_floor=8e-3)
-            tight = np.abs(got - ref) <= G.bf16_ulp(ref) + 2e-5
-            assert tight.mean() >= 0.999, f"{name}: {100 * (1 - tight.mean()):.3f}% beyond one ulp"
-        G.assert_ulps(f"v[{b}]", ob.widen_bf16(vb[b][:, sel]), qkv[2], ulps=1.0, abs_floor=2e-6 * np.sqrt(d))
+            G.say(f"  {name}: {100 * np.mean(got == ob.round_bf16(ref)):.2f}% equal to the rounded reference")
+            gates.check_qkv_pack(name, got, ref)
+        G.assert_ulps(f"v[{b}]", ob.widen_bf16(vb[b][:, sel]), rv, ulps=1.0, abs_floor=2e-6 * np.sqrt(d))
     assert np.all(qb[:, :, rows:] == 0) and np.all(kb[:, :, rows:] == 0) and np.all(vpad == 0)
 
 
 # ---- a5 attention -------------------------------------------------------------------------------------
 
-def _attention_case(batch, heads, rows, n_txt, lens, seed, q_scale=1.0, qkv_bits=None):
+def _attention_case(batch, heads, rows, n_txt, lens, seed, q_scale=1.0, qkv_bits=None, pad_dominant=False,
+                    ref_heads=None):
     if qkv_bits is None:
-        q = synth.make_tensor(seed, 0, (batch, heads, rows, 128), std=q_scale)
-        k = synth.make_tensor(seed, 1, (batch, heads, rows, 128))
-        v = synth.make_tensor(seed, 2, (batch, heads, rows, 128), std=1.3)
+        q, k, v = gates.attention_inputs(batch, heads, rows, seed, q_scale, n_txt, lens, pad_dominant)
     else:
         q, k, v = qkv_bits
     rp = moss.moss_packed_rows(rows)
@@ -301,11 +284,10 @@ def _attention_case(batch, heads, rows, n_txt, lens, seed, q_scale=1.0, qkv_bits
                           G.dev(G.pack_v(v, rp)), o)
     G.sync()
     got = G.host_f64(o).reshape(batch, rows, heads, 128).transpose(0, 2, 1, 3)
-    refs = []
-    for b in range(batch):
-        valid = ob.key_mask(n_txt, rows - n_txt, [lens[b] if lens is not None else n_txt])[0]
-        refs.append(ob.attention(ob.widen_bf16(q[b]), ob.widen_bf16(k[b]), ob.widen_bf16(v[b]), valid))
-    return got, np.stack(refs)
+    if ref_heads is not None:  # the oracle for these heads only (all heads still run on the GPU)
+        hs = list(ref_heads)
+        return got[:, hs], gates.attention_reference(q[:, hs], k[:, hs], v[:, hs], n_txt, lens)
+    return got, gates.attention_reference(q, k, v, n_txt, lens)
 
 
 @pytest.mark.parametrize("batch,heads,rows,n_txt,lens", [
@@ -318,14 +300,35 @@ def _attention_case(batch, heads, rows, n_txt, lens, seed, q_scale=1.0, qkv_bits
 def test_attention(batch, heads, rows, n_txt, lens):
     G.say(f"attention B={batch} H={heads} rows={rows} n_txt={n_txt} lens={lens}")
     got, ref = _attention_case(batch, heads, rows, n_txt, lens, seed=7)
-    G.assert_parity("o", got, ref, cos_min=0.99995, rel_max=1e-2)
+    gates.check_attention(got, ref)
 
 
 def test_attention_sharp_logits():
     """Logits about N(0, 16): exercises the running-max rescale."""
     G.say("attention sharp logits")
     got, ref = _attention_case(1, 2, 1000, 10, None, seed=8, q_scale=4.0)
-    G.assert_parity("o", got, ref, cos_min=0.99995, rel_max=1e-2)
+    gates.check_attention(got, ref)
+
+
+@pytest.mark.parametrize("batch,heads,rows,n_txt,lens", [
+    (2, 2, 4130, 34, (34, 10)),   # the guidance pair: 24 pad keys in item 2
+    (2, 3, 200, 150, (1, 149)),   # 149 and 1 pad keys, straddling 64-key tiles
+])
+def test_attention_pad_keys_dominant(batch, heads, rows, n_txt, lens):
+    """Pad keys that would win every query's softmax if let through: the key mask must hold exactly
+    (one pad key unmasked moves the output by about its value, 4)."""
+    G.say(f"attention pad-dominant B={batch} H={heads} rows={rows} lens={lens}")
+    got, ref = _attention_case(batch, heads, rows, n_txt, lens, seed=9, pad_dominant=True)
+    gates.check_attention(got, ref)
+
+
+@pytest.mark.parametrize("batch,lens", [(1, None), (2, (34, 10))])
+def test_attention_24_heads(batch, lens):
+    """The real head count at 4096+34 rows (408 and 816 workgroups, the XCD-ordered schedule): all 24
+    heads run; heads 0, 11 and 23 of each item are compared element by element with the oracle."""
+    G.say(f"attention 24 heads B={batch} lens={lens}")
+    got, ref = _attention_case(batch, 24, 4130, 34, lens, seed=11, ref_heads=(0, 11, 23))
+    gates.check_attention(got, ref)
 
 
 def test_attention_cancellation():
