@@ -55,10 +55,8 @@
 
 namespace {
 
-// fragment reads issued ahead of the MFMAs of a matrix step (0: the compiler's own order)
-#ifndef MOSS_ATTN_SCHED
-#define MOSS_ATTN_SCHED 4
-#endif
+// fragment reads issued ahead of the MFMAs of a matrix step (deeper lookahead, 6 or 8, changed nothing)
+constexpr int kReadsAhead = 4;
 
 constexpr int NWV = 8;           // wavefronts per workgroup, 32 queries each: two groups of four
 constexpr int BQ = 32 * NWV;     // queries per workgroup
@@ -275,15 +273,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(const uint16_t* _
     __builtin_amdgcn_s_setprio(1);
     pv(t - 1);
     qk(t);
-#if MOSS_ATTN_SCHED
-    __builtin_amdgcn_sched_group_barrier(0x100, MOSS_ATTN_SCHED, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kReadsAhead, 0);
 #pragma unroll
-    for (int q = 0; q < 32 - MOSS_ATTN_SCHED; ++q) {
+    for (int q = 0; q < 32 - kReadsAhead; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, MOSS_ATTN_SCHED, 0);
-#endif
+    __builtin_amdgcn_sched_group_barrier(0x008, kReadsAhead, 0);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
   };

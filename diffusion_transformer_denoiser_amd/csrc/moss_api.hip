@@ -244,6 +244,13 @@ bool weights_ok(const moss_block_weights* w) {
   return true;
 }
 
+// Does any of a block's weight tensors overlap the byte range [p, p + n)?
+bool weights_overlap(const moss_block_weights& w, const void* p, size_t n, size_t D, size_t F) {
+  return overlaps(p, n, w.w_mod, 2 * 6 * D * D) || overlaps(p, n, w.w_qkv, 2 * 3 * D * D) ||
+         overlaps(p, n, w.q_gain, 256) || overlaps(p, n, w.k_gain, 256) || overlaps(p, n, w.w_out, 2 * D * D) ||
+         overlaps(p, n, w.w_up, 2 * 2 * F * D) || overlaps(p, n, w.w_down, 2 * D * F);
+}
+
 // Validation shared by the block and the stack; fills ctx on success.
 int validate_forward(const moss_dims* d, int n_blocks, const uint16_t* x, const uint16_t* txt,
                      const int32_t* txt_len, const uint16_t* cond, const moss_block_weights* blocks,
@@ -264,14 +271,15 @@ int validate_forward(const moss_dims* d, int n_blocks, const uint16_t* x, const 
       overlaps(out, out_bytes, cond, 2 * B * D) || overlaps(out, out_bytes, rope, 4 * 2 * T * 64) ||
       overlaps(out, out_bytes, workspace, ctx->L.total))
     return MOSS_EALIAS;
-  for (int i = 0; i < n_blocks; ++i) {
-    const moss_block_weights& w = blocks[i];
-    if (overlaps(out, out_bytes, w.w_mod, 2 * 6 * D * D) || overlaps(out, out_bytes, w.w_qkv, 2 * 3 * D * D) ||
-        overlaps(out, out_bytes, w.q_gain, 256) || overlaps(out, out_bytes, w.k_gain, 256) ||
-        overlaps(out, out_bytes, w.w_out, 2 * D * D) || overlaps(out, out_bytes, w.w_up, 2 * 2 * F * D) ||
-        overlaps(out, out_bytes, w.w_down, 2 * D * F))
-      return MOSS_EALIAS;
-  }
+  for (int i = 0; i < n_blocks; ++i)
+    if (weights_overlap(blocks[i], out, out_bytes, D, F)) return MOSS_EALIAS;
+  // an input inside the workspace would be overwritten while it is still needed
+  if (overlaps(workspace, ctx->L.total, x, 2 * B * d->n_img * D) ||
+      overlaps(workspace, ctx->L.total, txt, 2 * B * d->n_txt * D) ||
+      overlaps(workspace, ctx->L.total, cond, 2 * B * D) || overlaps(workspace, ctx->L.total, rope, 4 * 2 * T * 64))
+    return MOSS_EALIAS;
+  for (int i = 0; i < n_blocks; ++i)
+    if (weights_overlap(blocks[i], workspace, ctx->L.total, D, F)) return MOSS_EALIAS;
   ctx->d = d;
   ctx->ws = static_cast<char*>(workspace);
   return MOSS_OK;
@@ -401,14 +409,13 @@ int denoiser(const moss_dims* d, int n_blocks, const uint16_t* latent, const uin
                         2 * D * D, 2 * D * ed, 2 * D * kLatent, 2 * 2 * D * D, 2 * kLatent * D};
   for (int i = 0; i < 10; ++i)
     if (overlaps(velocity, vb, in[i], len[i])) return MOSS_EALIAS;
-  for (int i = 0; i < n_blocks; ++i) {
-    const moss_block_weights& w = blocks[i];
-    if (overlaps(velocity, vb, w.w_mod, 2 * 6 * D * D) || overlaps(velocity, vb, w.w_qkv, 2 * 3 * D * D) ||
-        overlaps(velocity, vb, w.q_gain, 256) || overlaps(velocity, vb, w.k_gain, 256) ||
-        overlaps(velocity, vb, w.w_out, 2 * D * D) || overlaps(velocity, vb, w.w_up, 2 * 2 * F * D) ||
-        overlaps(velocity, vb, w.w_down, 2 * D * F))
-      return MOSS_EALIAS;
-  }
+  for (int i = 0; i < n_blocks; ++i)
+    if (weights_overlap(blocks[i], velocity, vb, D, F)) return MOSS_EALIAS;
+  // no input inside the workspace (in[3] is the workspace itself)
+  for (int i = 0; i < 10; ++i)
+    if (i != 3 && overlaps(workspace, E.total, in[i], len[i])) return MOSS_EALIAS;
+  for (int i = 0; i < n_blocks; ++i)
+    if (weights_overlap(blocks[i], workspace, E.total, D, F)) return MOSS_EALIAS;
   int rc = check_current_device();
   if (rc != MOSS_OK) return rc;
   c.d = d;
@@ -462,7 +469,7 @@ const char* moss_status_string(int status) {
   switch (status) {
     case MOSS_OK: return "ok";
     case MOSS_EINVAL: return "invalid argument";
-    case MOSS_EALIAS: return "an output overlaps an input or the workspace";
+    case MOSS_EALIAS: return "an output overlaps an input or the workspace, or an input lies in the workspace";
     case MOSS_EWORKSPACE: return "workspace missing or too small";
     case MOSS_EDEVICE: return "no gfx950 device";
     case MOSS_EHIP: return g_hip_error.empty() ? "HIP error" : g_hip_error.c_str();

@@ -44,7 +44,7 @@ extern "C" {
 /* ---- status codes -------------------------------------------------------- */
 #define MOSS_OK 0
 #define MOSS_EINVAL 1     /* a bad argument: null pointer, bad shape, misalignment, bad txt_len, eps <= 0 */
-#define MOSS_EALIAS 2     /* an output overlaps an input or the workspace */
+#define MOSS_EALIAS 2     /* an output overlaps an input or the workspace, or an input lies in the workspace */
 #define MOSS_EWORKSPACE 3 /* workspace null or smaller than moss_workspace_bytes() */
 #define MOSS_EDEVICE 4    /* no HIP device, or the device is not gfx950 */
 #define MOSS_EHIP 5       /* a HIP launch failed; moss_status_string() holds the text */
@@ -116,7 +116,9 @@ int moss_rope_build(int32_t n_txt, int32_t grid_h, int32_t grid_w, float theta, 
  *   rope    [2][T][64] fp32 tables as moss_rope_build writes them
  *   out     [B, T, D] block output (bf16), text rows first; must not overlap
  *           any input or the workspace
- *   workspace, ws_bytes: device scratch of at least moss_workspace_bytes(dims, 1)
+ *   workspace, ws_bytes: device scratch of at least moss_workspace_bytes(dims, 1);
+ *           no input or weight may lie in it (the call overwrites it while the
+ *           inputs are still needed): MOSS_EALIAS
  * Computes, per item, h0 = [txt; x], mod = W_mod SiLU(cond), a = RMSNorm(h0)
  * (1 + scale1) + shift1, qkv = a W_qkv^T, per head q/k RMSNorm x gain and
  * rotary, O = softmax(q k^T / sqrt(128) + mask) v, h1 = h0 + gate1 (O W_out^T),
@@ -206,7 +208,8 @@ size_t moss_denoiser_workspace_bytes(const moss_dims* dims, int32_t n_blocks);
  * pipeline's timestep scale, e.g. 1000 sigma), velocity [B, n_img, 128] bf16,
  * all device pointers 16-byte aligned.  rope, txt_len, blocks and the error
  * codes as moss_stack_forward; velocity must not overlap any input, weight
- * or the workspace (MOSS_EALIAS); n_img >= 1. */
+ * or the workspace, and no input or weight may lie in the workspace
+ * (MOSS_EALIAS); n_img >= 1. */
 int moss_denoiser_forward(const moss_dims* dims, int32_t n_blocks, const uint16_t* latent, const uint16_t* enc,
                           const int32_t* txt_len, const float* t, const moss_denoiser_weights* ends,
                           const moss_block_weights* blocks, const uint8_t* skip, const float* rope,

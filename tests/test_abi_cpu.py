@@ -128,6 +128,24 @@ def test_block_rejects_aliasing():
     assert block(d, out=fake(14, 1 << 20)) == moss.MOSS_EALIAS  # out overlaps w_out
 
 
+@pytest.mark.parametrize("which", ["x", "txt", "cond", "rope"])
+def test_block_rejects_input_in_workspace(which):
+    """An input that lies in the workspace would be overwritten during the call."""
+    assert block(c2_dims(), **{which: fake(6, 1 << 20)}) == moss.MOSS_EALIAS
+
+
+def test_block_rejects_weights_in_workspace():
+    w = weights()
+    w.w_down = fake(6, 4 << 20)
+    assert block(c2_dims(), w=w) == moss.MOSS_EALIAS
+    L = moss.lib()
+    ws = (moss.moss_block_weights * 2)(weights(), weights(20))
+    ws[1].q_gain = fake(6, 256)
+    d = c2_dims()
+    assert L.moss_stack_forward(ctypes.byref(d), 2, fake(1), fake(2), None, fake(3), ws, fake(4), fake(5), fake(6),
+                                moss.moss_workspace_bytes(d, 2), None) == moss.MOSS_EALIAS
+
+
 def test_valid_call_without_gpu_reports_device():
     """With valid arguments the call reaches the device check; here there is no GPU."""
     if moss.moss_device_check(0) == moss.MOSS_OK:
@@ -269,5 +287,9 @@ def test_denoiser_validates():
     assert denoiser(d, vel=fake(6, 4096)) == moss.MOSS_EALIAS  # velocity inside the workspace
     assert denoiser(d, vel=fake(1, 256)) == moss.MOSS_EALIAS  # velocity over the latent
     assert denoiser(d, vel=fake(35, 0)) == moss.MOSS_EALIAS  # velocity over w_final
+    assert denoiser(d, latent=fake(6, 4096)) == moss.MOSS_EALIAS  # latent inside the workspace
+    e = _ends()
+    e.w_t2 = fake(6, 1 << 20)
+    assert denoiser(d, ends=e) == moss.MOSS_EALIAS  # a weight of the ends inside the workspace
     if moss.moss_device_check(0) != moss.MOSS_OK:
         assert denoiser(d) == moss.MOSS_EDEVICE
