@@ -458,6 +458,50 @@ int denoiser(const moss_dims* d, int n_blocks, const uint16_t* latent, const uin
 
 int single_device_check() { return check_current_device(); }
 
+// ---- the block forward for callers that cannot allocate ----------------------------
+// Its workspace is this file-scope array: one copy per GPU, held from the library's load to the
+// end of the process.  Host code never passes the array's name to a kernel (in host code it is a
+// host-side stand-in, not a device address): each device's address comes from
+// hipGetSymbolAddress, once per device with that device current, and only that address is used.
+constexpr size_t kScratchBytes = (size_t)MOSS_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) __attribute__((used)) char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // per device; null until looked up
+
+int scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOSS_EDEVICE;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return hip_fail(hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOSS_OK;
+}
+
+int forward_noalloc(const moss_dims* d, const uint16_t* x, const uint16_t* txt, const int32_t* txt_len,
+                    const uint16_t* cond, const moss_block_weights* w, const float* rope, uint16_t* out,
+                    hipStream_t st) {
+  // the size limit first, before any HIP call
+  if (!dims_ok(d)) return MOSS_EINVAL;
+  if (plan(d, 1).total > kScratchBytes) return MOSS_EWORKSPACE;
+  int rc = check_current_device();
+  if (rc != MOSS_OK) return rc;
+  void* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc != MOSS_OK) return rc;
+  Ctx c;
+  rc = validate_forward(d, 1, x, txt, txt_len, cond, w, rope, out, ws, kScratchBytes, &c);
+  if (rc != MOSS_OK) return rc;
+  c.st = st;
+  return run_stack(c, 1, x, txt, cond, w, rope, out, nullptr);
+}
+
 }  // namespace
 
 // ============================================================================
@@ -501,6 +545,14 @@ int moss_block_forward(const moss_dims* dims, const uint16_t* x, const uint16_t*
                        void* workspace, size_t ws_bytes, hipStream_t stream) {
   return forward(dims, 1, x, txt, txt_len, cond, w, rope, out, workspace, ws_bytes, stream);
 }
+
+int moss_block_forward_noalloc(const moss_dims* dims, const uint16_t* x, const uint16_t* txt,
+                               const int32_t* txt_len, const uint16_t* cond, const moss_block_weights* w,
+                               const float* rope, uint16_t* out, hipStream_t stream) {
+  return forward_noalloc(dims, x, txt, txt_len, cond, w, rope, out, stream);
+}
+
+size_t moss_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int moss_stack_forward(const moss_dims* dims, int32_t n_blocks, const uint16_t* x, const uint16_t* txt,
                        const int32_t* txt_len, const uint16_t* cond, const moss_block_weights* blocks,

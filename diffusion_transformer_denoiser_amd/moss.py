@@ -60,6 +60,9 @@ _SIGS = {
     "moss_rope_build": (ctypes.c_int, [c_i32, c_i32, c_i32, c_f32, c_vp, c_vp]),
     "moss_block_forward": (ctypes.c_int, [ctypes.POINTER(moss_dims), c_vp, c_vp, c_vp, c_vp,
                                           ctypes.POINTER(moss_block_weights), c_vp, c_vp, c_vp, c_size, c_vp]),
+    "moss_block_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(moss_dims), c_vp, c_vp, c_vp, c_vp,
+                                                  ctypes.POINTER(moss_block_weights), c_vp, c_vp, c_vp]),
+    "moss_noalloc_scratch_bytes": (c_size, []),
     "moss_stack_forward": (ctypes.c_int, [ctypes.POINTER(moss_dims), c_i32, c_vp, c_vp, c_vp, c_vp,
                                           ctypes.POINTER(moss_block_weights), c_vp, c_vp, c_vp, c_size, c_vp]),
     "moss_stack_forward_skip": (ctypes.c_int, [ctypes.POINTER(moss_dims), c_i32, c_vp, c_vp, c_vp, c_vp,
@@ -191,6 +194,17 @@ def moss_block_forward(dims, x, txt, txt_len, cond, weights, rope, out, workspac
                                   workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                   _s(stream))
     _check(rc, "moss_block_forward")
+
+
+def moss_block_forward_noalloc(dims, x, txt, txt_len, cond, weights, rope, out, stream=None) -> None:
+    w = weights if isinstance(weights, moss_block_weights) else make_weights(weights)
+    rc = lib().moss_block_forward_noalloc(ctypes.byref(dims), _p(x), _p(txt), ctypes.cast(_lens(txt_len), c_vp),
+                                          _p(cond), ctypes.byref(w), _p(rope), _p(out), _s(stream))
+    _check(rc, "moss_block_forward_noalloc")
+
+
+def moss_noalloc_scratch_bytes() -> int:
+    return int(lib().moss_noalloc_scratch_bytes())
 
 
 def moss_stack_forward(dims, blocks, x, txt, txt_len, cond, rope, out, workspace, stream=None) -> None:

@@ -133,6 +133,26 @@ int moss_block_forward(const moss_dims* dims, const uint16_t* x, const uint16_t*
                        const float* rope, uint16_t* out, void* workspace, size_t ws_bytes,
                        hipStream_t stream);
 
+/* moss_block_forward for callers that cannot allocate or be handed device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments and results (byte for byte) as
+ * moss_block_forward, without the workspace: the call uses a scratch array of
+ * MOSS_NOALLOC_SCRATCH_BYTES (256 MiB) that the library holds in each GPU's
+ * memory from its load to the end of the process, and calls no hipMalloc or
+ * hipFree.  A geometry whose workspace (moss_workspace_bytes(dims, 1)) exceeds
+ * that returns MOSS_EWORKSPACE: one block at up to 4096 + 34 rows at batch 1
+ * (4188 rows: 248 MiB) or about 2 x 2100 rows at D = 3072 fits.  Every call on
+ * one GPU shares that GPU's array, which keeps the last call's contents: calls
+ * that overlap on one GPU (other streams, other threads) race and must not be
+ * issued.  The call writes every scratch byte it reads first, so nothing needs
+ * clearing between calls.  Other codes as moss_block_forward. */
+#define MOSS_NOALLOC_SCRATCH_BYTES (256u << 20)
+int moss_block_forward_noalloc(const moss_dims* dims, const uint16_t* x, const uint16_t* txt,
+                               const int32_t* txt_len, const uint16_t* cond, const moss_block_weights* w,
+                               const float* rope, uint16_t* out, hipStream_t stream);
+/* The scratch limit above, in bytes. */
+size_t moss_noalloc_scratch_bytes(void);
+
 /* n_blocks block forwards in sequence (blocks: host array of n_blocks weight
  * structs), each on the previous block's output, with the same cond, rope and
  * txt_len.  Arguments otherwise as moss_block_forward; `out` holds the

@@ -293,3 +293,18 @@ def test_denoiser_validates():
     assert denoiser(d, ends=e) == moss.MOSS_EALIAS  # a weight of the ends inside the workspace
     if moss.moss_device_check(0) != moss.MOSS_OK:
         assert denoiser(d) == moss.MOSS_EDEVICE
+
+
+def test_noalloc_block_validates():
+    """The no-allocation block forward: a geometry whose workspace exceeds the library's scratch is
+    refused before any HIP call; a fitting one reaches the device check (no GPU here)."""
+    L = moss.lib()
+    assert moss.moss_noalloc_scratch_bytes() == 256 << 20
+    big = c2_dims(batch=2)
+    assert moss.moss_workspace_bytes(big, 1) > moss.moss_noalloc_scratch_bytes()
+    args = (fake(1), fake(2), None, fake(3), ctypes.byref(weights()), fake(4), fake(5), None)
+    assert L.moss_block_forward_noalloc(ctypes.byref(big), *args) == moss.MOSS_EWORKSPACE
+    bad = c2_dims(d_model=3000)
+    assert L.moss_block_forward_noalloc(ctypes.byref(bad), *args) == moss.MOSS_EINVAL
+    if moss.moss_device_check(0) != moss.MOSS_OK:
+        assert L.moss_block_forward_noalloc(ctypes.byref(c2_dims()), *args) == moss.MOSS_EDEVICE
