@@ -8,6 +8,14 @@ second gated residual add in its epilogue) on one batch of seeded synthetic
 inputs already resident in HBM: D = 3072, 24 heads x 128, MLP 12288, a 64x64
 image grid plus 34 text rows (the 1024x1024 picture's shape on the
 MOSS-Image transformer page, "Measured"), weights N(0, 0.02).
+``--workload p1280|p1408|p1536`` times the larger pictures instead (5120,
+5632 and 6144 image rows).
+
+Each timed step has its own pair of HIP events on the launch stream;
+``ms_per_step`` is the median over the steps (the pages report the median of
+100 forwards), with p10 / p90 beside it, and ``value`` = 1000 / median.
+Every timed step's output is compared on the GPU with the first one's (outside
+the event pairs), and the line says whether all were byte-identical.
 
 Prints one JSON line.  ``roofline`` is for the up projection (the largest
 kernel, 43% of the block's flops), timed live with HIP events recorded by the
@@ -15,19 +23,22 @@ library around each of its launches inside the timed region.  Its ``traffic``
 (HBM bytes per launch) comes from the committed FETCH_SIZE / WRITE_SIZE
 counter summary under ``profiles/`` when that summary was taken on the GEMM
 source as it is now, else it is null.  ``cpu_baseline`` times the float64
-oracle on one block forward of the same workload.
+oracle on block forwards of the same workload.
 
 After the main timing (unless ``--no-extras``) the line also carries: each
-step's launch time inside block forwards (the library's probe), warm and with
-the 256 MB Infinity Cache flushed before every forward; whether five repeated
-outputs hash identically; the 24-block guidance-pair stack (two items of 4096
-image + 34 text rows) in ms per call; and the block replayed from a captured
-HIP graph.
+step's launch time inside block forwards (the library's probe) with its
+fraction of the MFMA or HBM peak, warm and with the 256 MB Infinity Cache
+flushed before every forward; the 24-block guidance-pair stack (two items of
+4096 image + 34 text rows) in ms per call; the larger pictures (block and
+attention time against the square of the row count); and the block replayed
+from a captured HIP graph.
 
 Counter runs: ``--copy-calibration`` adds one plain 256 MiB device copy before
 the warm-up, so that each ``rocprofv3 --pmc`` run also records what the
 counter reads for a known byte count.  ``--traffic-summary FETCH_DIR
 WRITE_DIR`` (no GPU) turns the two runs' counter CSVs into the summary file.
+``--counter-summary DIR...`` (no GPU) writes the MFMA / LDS / wait counter
+summary from ``rocprofv3 --pmc`` CSV runs.
 """
 from __future__ import annotations
 
@@ -48,7 +59,7 @@ PEAK_HBM_GBS = 8000.0
 CALIB_BYTES = 256 << 20  # the plain device copy the counters are scaled by
 PROBE_EVERY = 5  # the timed steps whose up projection the probe brackets: 0, 5, 10, ...
 # the up projection with the SiLU gate epilogue: whole 256-row tiles, then the 34 leftover rows as 64 x 128 tiles
-UP_KERNELS = ("gemm_nt_kernel<256, 256, 2, 4, 1, 5>", "gemm_nt_kernel<64, 128, 2, 2, 1, 4>")
+UP_KERNELS = ("gemm_nt_kernel<256, 256, 2, 4, 1>", "gemm_nt_kernel<64, 128, 2, 2, 1>")
 GEMM_SOURCES = ("diffusion_transformer_denoiser_amd/csrc/gemm.hip", "diffusion_transformer_denoiser_amd/csrc/common.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_up_c2_traffic.md")
 METRIC = "denoiser block-forwards/s and TFLOP/s at 4096+34 tokens; MFMA % of peak"
@@ -57,8 +68,10 @@ METRIC = "denoiser block-forwards/s and TFLOP/s at 4096+34 tokens; MFMA % of pea
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="c2", choices=("c2", "p1280", "p1408", "p1536"),
+                   help="the timed block: 4096 image rows (default) or a larger picture")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-extras", action="store_true",
@@ -69,6 +82,10 @@ def parse():
                    help="time the float64 oracle on the c0-c3 blocks and two c4 blocks (CPU only), then exit")
     p.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="write the HBM traffic summary from two rocprofv3 --pmc CSV runs, then exit")
+    p.add_argument("--trace-summary", metavar="DB",
+                   help="print the per-kernel table of a rocprofv3 --kernel-trace database (results.db), then exit")
+    p.add_argument("--counter-summary", nargs="+", metavar="DIR",
+                   help="write the MFMA / LDS / wait counter summary from rocprofv3 --pmc CSV runs, then exit")
     return p.parse_args()
 
 
@@ -198,6 +215,113 @@ def traffic_summary(fetch_dir, write_dir, geom):
     print("\n".join(lines))
 
 
+def trace_summary(db):
+    """Per kernel of a rocprofv3 --kernel-trace database: shape, registers, LDS, dispatches and
+    durations (the registers and LDS as the code object records them)."""
+    import sqlite3
+    c = sqlite3.connect(db)
+    rows = c.execute(
+        "select s.display_name, d.grid_size_x, d.grid_size_y, d.workgroup_size_x, s.arch_vgpr_count, "
+        "s.accum_vgpr_count, s.group_segment_size, count(*), avg(d.end - d.start), min(d.end - d.start), "
+        "max(d.end - d.start), sum(d.end - d.start) from rocpd_kernel_dispatch d join rocpd_info_kernel_symbol s "
+        "on d.kernel_id = s.id group by s.display_name, d.grid_size_x, d.grid_size_y order by sum(d.end - d.start) desc"
+    ).fetchall()
+    total = sum(r[11] for r in rows)
+    print("| kernel | grid (threads) | block | VGPR | AGPR | LDS B | calls | avg us | min us | max us | share |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    for name, gx, gy, bx, vg, ag, lds, n, avg, mn, mx, tot in rows:
+        short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        print(f"| {short} | {gx}x{gy} | {bx} | {vg} | {ag} | {lds} | {n} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | "
+              f"{mx / 1e3:.1f} | {100 * tot / total:.1f}% |")
+
+
+COUNTER_FILE = os.path.join(ROOT, "profiles", "mfma_util_c2.md")
+COUNTER_PASSES = (
+    "GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY "
+    "SQ_ACTIVE_INST_ANY SQ_INSTS_MFMA",
+    "GRBM_GUI_ACTIVE SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS "
+    "SQ_LDS_DATA_FIFO_FULL SQ_INSTS_VALU_MFMA_MOPS_BF16",
+)
+
+
+def counter_summary(dirs):
+    """Per kernel of a block forward: the MFMA, wait and LDS counters of rocprofv3 --pmc runs (each
+    with --kernel-trace, so every dispatch has its duration), averaged over the dispatches."""
+    import csv
+    import glob
+    per = {}   # (kernel, grid) -> counter -> [values]
+    dur = {}   # (kernel, grid) -> [ns]
+    n_xcc, n_simd = 8, 1024
+    for folder in dirs:
+        cc = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+        kt = glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True)
+        ag = glob.glob(os.path.join(folder, "**", "*agent_info.csv"), recursive=True)
+        if len(cc) != 1 or len(kt) != 1:
+            raise SystemExit(f"{folder}: expected one counter_collection.csv and one kernel_trace.csv")
+        for r in (csv.DictReader(open(ag[0])) if ag else []):
+            if r.get("Agent_Type", r.get("Type", "")).upper().endswith("GPU"):
+                n_xcc = int(r.get("Num_Xcc", n_xcc) or n_xcc)
+                n_simd = int(r.get("Simd_Count", 0) or 0) or n_simd
+        times = {r["Dispatch_Id"]: int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in csv.DictReader(open(kt[0]))}
+        for r in csv.DictReader(open(cc[0])):
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+            if name.startswith("__amd") or name.startswith("at::"):
+                continue
+            key = (name, int(r["Grid_Size"]))
+            per.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE" and r["Dispatch_Id"] in times:
+                dur.setdefault(key, []).append(times[r["Dispatch_Id"]])
+    lines = [
+        "# MFMA, wait and LDS counters per kernel of a block forward at 4096 image + 34 text rows",
+        "",
+        "Commands (on one MI355X, from the repository root; one counter pass per run, each with the kernel",
+        "trace so that every dispatch has its duration):",
+        "",
+    ]
+    for i, ctrs in enumerate(COUNTER_PASSES):
+        lines.append(f"    rocprofv3 --pmc {ctrs} --kernel-trace --output-format csv -d gpurun_out/pmc_sq{i} -o run "
+                     "-- python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-extras")
+    lines += ["    python3 bench.py --counter-summary " + " ".join(f"gpurun_out/pmc_sq{i}" for i in range(len(COUNTER_PASSES))),
+              "",
+              f"Values are per dispatch, averaged over the dispatches of each kernel ({n_xcc} XCDs, {n_simd} SIMDs).  "
+              "`GRBM_GUI_ACTIVE` sums the XCDs' busy cycles, so the clock is GRBM_GUI_ACTIVE / XCDs / duration.  "
+              "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x SIMDs) (rocprofv3's MfmaUtil).  "
+              "Wait = SQ_WAIT_ANY / SQ_WAVE_CYCLES (wave cycles at a wait count or barrier); issue-blocked = "
+              "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES.  LDS busy = SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE / XCDs x CUs) "
+              "(rocprofv3's LdsUtil); bank conflicts are cycles per LDS-active cycle.  MFMA TFLOP/s = "
+              "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / duration.  The counters cover the collection window around a "
+              "dispatch, a few microseconds longer than the kernel: for kernels of tens of microseconds the clock "
+              "reads high (above the 2.4 GHz maximum) and the busy fractions are diluted by the same factor.",
+              "",
+              "| kernel | grid | dispatches | avg us | clock GHz | MFMA busy | wait | issue-blocked | LDS busy | "
+              "bank conflict | MFMA TFLOP/s |",
+              "|---|---|---|---|---|---|---|---|---|---|---|"]
+    n_cu = n_simd // 4
+
+    def avg(d, c):
+        v = d.get(c)
+        return float(np.mean(v)) if v else float("nan")
+
+    order = sorted(per, key=lambda k: -float(np.mean(dur.get(k, [0]))))
+    for key in order:
+        d = per[key]
+        us = float(np.mean(dur[key])) / 1e3 if key in dur else float("nan")
+        gui = avg(d, "GRBM_GUI_ACTIVE") / n_xcc
+        clock = gui / (us * 1e3) if us == us else float("nan")
+        mfma = avg(d, "SQ_VALU_MFMA_BUSY_CYCLES") / (gui * n_simd)
+        wait = avg(d, "SQ_WAIT_ANY") / avg(d, "SQ_WAVE_CYCLES")
+        blocked = avg(d, "SQ_WAIT_INST_ANY") / avg(d, "SQ_WAVE_CYCLES")
+        lds = avg(d, "SQ_LDS_IDX_ACTIVE") / (gui * n_cu)
+        conf = avg(d, "SQ_LDS_BANK_CONFLICT") / max(avg(d, "SQ_LDS_IDX_ACTIVE"), 1.0)
+        tf = avg(d, "SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512 / (us * 1e-6) / 1e12 if us == us else float("nan")
+        lines.append(f"| {key[0]} | {key[1]} | {len(dur.get(key, []))} | {us:.1f} | {clock:.2f} | {100 * mfma:.1f}% | "
+                     f"{100 * wait:.1f}% | {100 * blocked:.1f}% | {100 * lds:.1f}% | {conf:.3f} | {tf:.0f} |")
+    lines.append("")
+    with open(COUNTER_FILE, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def cpu_baseline(geom, acts, wbits, min_seconds=10.0, max_forwards=8):
     """Time the float64 oracle on whole block forwards of the same workload: repeated until about
     min_seconds of CPU work (at most max_forwards), so the sample is bounded but not one noisy call."""
@@ -220,6 +344,7 @@ def cpu_baseline(geom, acts, wbits, min_seconds=10.0, max_forwards=8):
 # the steps that launch kernels of their own (the q/k norm and packing, the gated adds and the SiLU
 # product run in GEMM epilogues)
 PROBED = ("JOIN", "ADALN", "NORM1", "QKV", "ATTN", "OUT", "NORM2", "UP", "DOWN")
+MFMA_STEPS = ("QKV", "ATTN", "OUT", "UP", "DOWN")
 # algorithmic work per step at one block forward of this workload: (GFLOP, MB)
 def step_work(geom):
     m, d, f = geom.batch * geom.rows, geom.d_model, geom.mlp_inner
@@ -262,19 +387,90 @@ def per_step(torch, moss, step, geom, reps=5, cold=False):
             entry["tflops"] = round(gflop / us * 1e3, 1)
         if mb:
             entry["gb_s"] = round(mb / us * 1e3, 1)
+        # the fraction of the peak that bounds the step: MFMA for the contractions, HBM for the rest
+        if name in MFMA_STEPS:
+            entry["mfma_frac"] = round(gflop / us * 1e3 / PEAK_BF16_TFLOPS, 4)
+        elif mb:
+            entry["hbm_frac"] = round(mb / us * 1e3 / PEAK_HBM_GBS, 4)
         res[name.lower()] = entry
     return res
 
 
-def repeat_hashes(torch, step, out, reps=5):
-    """Every repeat's output hashed: all equal?"""
-    seen = set()
-    for _ in range(reps):
-        out.fill_(0)
+def timed_steps(torch, step, out, stream, steps):
+    """Run `steps` steps, each between its own pair of events on the launch stream.  After each
+    step (outside its events) its output is copied into a device ring; after the loop every copy
+    is compared with the first.  Returns (per-step ms, ms per step over the whole loop, wall
+    seconds, all outputs identical, sha256 of the first output)."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    loop0, loop1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ring = torch.empty((steps, *out.shape), dtype=out.dtype, device=out.device)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    loop0.record(stream)
+    for i in range(steps):
+        starts[i].record(stream)
         step()
+        ends[i].record(stream)
+        ring[i].copy_(out)
+    loop1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    identical = all(torch.equal(ring[i], ring[0]) for i in range(1, steps))
+    digest = hashlib.sha256(ring[0].cpu().numpy().tobytes()).hexdigest()[:16]
+    del ring
+    return ms, loop0.elapsed_time(loop1) / steps, wall, identical, digest
+
+
+def larger_pictures(torch, moss, w, seed, reps=20):
+    """Block and attention time at 4096 image rows and at the larger pictures of the CUDA port
+    page's served-picture table (1280x1024, 1408x1024, 1536x1024: 5120, 5632 and 6144 image
+    rows), with the attention time per square row relative to the 4096-row block."""
+    from diffusion_transformer_denoiser_amd import synth
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+
+    res = {}
+    base = None
+    for name in ("c2", "p1280", "p1408", "p1536"):
+        geom = synth.CONFIGS[name]
+        acts = synth.make_activations(geom, seed)
+        dims = moss.make_dims(geom.batch, geom.n_img, geom.n_txt, geom.d_model, geom.mlp_inner, geom.eps)
+        x, txt, cond = dev(acts["x"]), dev(acts["txt"]), dev(acts["cond"])
+        rope = torch.empty(2, geom.rows, 64, dtype=torch.float32, device="cuda")
+        moss.moss_rope_build(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, rope)
+        ws = torch.empty(moss.moss_workspace_bytes(dims, 1), dtype=torch.uint8, device="cuda")
+        out = torch.empty(geom.batch, geom.rows, geom.d_model, dtype=torch.int16, device="cuda")
+
+        def step():
+            moss.moss_block_forward(dims, x, txt, acts["txt_len"], cond, w, rope, out, ws)
+
+        for _ in range(3):
+            step()
+        ms, _, _, same, _ = timed_steps(torch, step, out, torch.cuda.current_stream(), reps)
+        moss.moss_probe_arm("ATTN", 5)
+        for _ in range(5):
+            step()
         torch.cuda.synchronize()
-        seen.add(hashlib.sha256(out.cpu().numpy().tobytes()).hexdigest())
-    return len(seen) == 1
+        attn_us = 1000.0 * float(np.mean(moss.moss_probe_collect(5)))
+        t = geom.rows
+        attn_gflop = 4.0 * geom.batch * geom.n_heads * t * t * 128 / 1e9
+        med = float(np.median(ms))
+        per_t2 = attn_us / (t * t)
+        if base is None:
+            base = per_t2
+        res[name] = {"image_rows": geom.n_img, "rows": t, "block_ms": round(med, 4),
+                     "block_forwards_s": round(1000.0 / med, 2),
+                     "block_tflops": round(geom.block_flops() / med / 1e9, 1),
+                     "attention_us": round(attn_us, 2), "attention_tflops": round(attn_gflop / attn_us * 1e3, 1),
+                     "attention_mfma_frac": round(attn_gflop / attn_us * 1e3 / PEAK_BF16_TFLOPS, 4),
+                     "attention_us_per_t2_vs_4096_rows": round(per_t2 / base, 4),
+                     "outputs_identical": same}
+        del ws, out, x, txt, cond, rope
+    torch.cuda.empty_cache()
+    return res
 
 
 def stack_timing(torch, moss, geom, seed, reps=3):
@@ -421,6 +617,12 @@ def main():
         from diffusion_transformer_denoiser_amd import synth
         traffic_summary(*args.traffic_summary, synth.CONFIGS["c2"])
         return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the block forward is "
               "measured on a single MI355X).", file=sys.stderr)
@@ -436,7 +638,7 @@ def main():
     if rc != moss.MOSS_OK:
         raise SystemExit(f"device 0: {moss.moss_status_string(rc)}")
 
-    geom = synth.CONFIGS["c2"]
+    geom = synth.CONFIGS[args.workload]
     acts = synth.make_activations(geom, args.seed)
     wbits = synth.make_block_weights(geom, args.seed, 0)
 
@@ -471,38 +673,32 @@ def main():
 
     # the up projection of every PROBE_EVERY-th timed step is bracketed by events (each record leaves
     # a few microseconds of stream time between kernels; spreading them keeps that out of most steps)
-    moss.moss_probe_arm("UP", max(1, args.steps // PROBE_EVERY), PROBE_EVERY)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    up_ms = moss.moss_probe_collect(max(1, args.steps // PROBE_EVERY))
-    ms = ev0.elapsed_time(ev1) / args.steps
-    digest = hashlib.sha256(out.cpu().numpy().tobytes()).hexdigest()[:16]
+    n_probe = max(1, (args.steps + PROBE_EVERY - 1) // PROBE_EVERY)
+    moss.moss_probe_arm("UP", n_probe, PROBE_EVERY)
+    step_ms, loop_ms, wall, identical, digest = timed_steps(torch, step, out, stream, args.steps)
+    up_ms = moss.moss_probe_collect(n_probe)
+    med = float(np.median(step_ms))
+    p10, p90 = (float(v) for v in np.percentile(step_ms, [10, 90]))
 
-    graph_ms = graph_timing(torch, step, stream, args.steps)
+    graph_ms = graph_timing(torch, step, stream, min(args.steps, 50))
     extras = {}
     if not args.no_extras:
-        print("bench: per-step times, repeat hashes, 24-block stack", file=sys.stderr, flush=True)
+        print("bench: per-step times, 24-block stack, larger pictures", file=sys.stderr, flush=True)
         extras["step_times"] = per_step(torch, moss, step, geom)
         extras["step_times_cold_cache"] = per_step(torch, moss, step, geom, cold=True)
-        extras["repeat_outputs_identical"] = repeat_hashes(torch, step, out)
         extras["stack_c4"] = stack_timing(torch, moss, synth.CONFIGS["c4"], args.seed)
+        extras["larger_pictures"] = larger_pictures(torch, moss, w, args.seed)
 
-    value = 1000.0 / ms
+    value = 1000.0 / med
     flops = geom.block_flops()
     tflops = flops * value / 1e12
     m = geom.batch * geom.rows
     up_flops = 2.0 * m * (2 * geom.mlp_inner) * geom.d_model
     up_avg_ms = float(np.mean(up_ms)) if up_ms else float("nan")
     up_tflops = up_flops / (up_avg_ms / 1e3) / 1e12
-    traffic = stored_traffic()
+    traffic = stored_traffic() if args.workload == "c2" else None
+    names = {"c2": "4096 image + 34 text rows (64x64 grid)", "p1280": "5120 image + 34 text rows (64x80 grid)",
+             "p1408": "5632 image + 34 text rows (64x88 grid)", "p1536": "6144 image + 34 text rows (64x96 grid)"}
 
     res = {
         "metric": METRIC,
@@ -511,8 +707,14 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": round(med, 4),
+        "ms_per_step_p10": round(p10, 4),
+        "ms_per_step_p90": round(p90, 4),
+        "ms_per_step_mean": round(float(np.mean(step_ms)), 4),
+        "ms_per_step_loop": round(loop_ms, 4),
         "wall_ms_per_step": round(wall * 1000 / args.steps, 4),
+        "timing": "median of the per-step HIP event pairs on the launch stream; p10 / p90 and the mean beside it; "
+                  "loop = one event pair around all steps (includes the copy of each output for the comparison)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -522,13 +724,15 @@ def main():
         "mfma_frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "block_gflop": round(flops / 1e9, 2),
         "output_sha256_16": digest,
+        "timed_outputs_identical": identical,
         "graph_ms_per_step": graph_ms,
         **extras,
-        "config": {"workload": "single DiT denoiser block forward, 4096 image + 34 text rows (64x64 grid), "
-                               "D=3072, 24 heads x 128, MLP inner 12288 SiLU-gated, batch 1",
+        "config": {"workload": f"single DiT denoiser block forward, {names[args.workload]}, D=3072, 24 heads x 128, "
+                               "MLP inner 12288 SiLU-gated, batch 1",
                    "global_batch": 1, "seq_len": geom.rows, "parallelism": "single GPU"},
-        "roofline": {"kernel": "up projection GEMM with the SiLU gate epilogue (4130 x 24576 x 3072; whole "
-                               "256-row tiles, then the 34 leftover rows as 64 x 128 tiles in a second launch, timed together)",
+        "roofline": {"kernel": f"up projection GEMM with the SiLU gate epilogue ({m} x {2 * geom.mlp_inner} x "
+                               f"{geom.d_model}; whole 256-row tiles, then the leftover rows as 64 x 128 tiles in a "
+                               "second launch, timed together)",
                      "bound": "mfma",
                      "achieved": round(up_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(up_tflops / PEAK_BF16_TFLOPS, 4),

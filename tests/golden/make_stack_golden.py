@@ -5,8 +5,10 @@ image + 34 text rows per item, the second item with 10 valid text rows (the
 empty negative prompt's length on the MOSS-Image encoder page, "Receipt").
 Inputs come from the seeded generator (seed 0).  Only the oracle computes
 here; the file it writes, ``stack24_c4_rows.npz``, is what the GPU stack test
-compares against.  About 2 minutes on a 16-core host (one block's float64
-weights are resident at a time).
+compares against: the sampled rows element by element, and a sketch of every
+row of both items (its norm, and its product with 16 fixed Gaussian
+directions, for the output and for the update out - h0).  About 2 minutes on
+a 16-core host (one block's float64 weights are resident at a time).
 
     python tests/golden/make_stack_golden.py [out.npz]
 """
@@ -29,6 +31,20 @@ from oracle import dit_block as ob  # noqa: E402
 # rows sampled per item: text rows (valid and, for item 1, padding), the first
 # and last image rows, and rows spread over the grid
 SAMPLE_ROWS = (0, 5, 9, 10, 20, 33, 34, 35, 97, 1000, 2081, 2082, 3000, 3333, 4096, 4129)
+
+
+SKETCH_DIM = 16
+SKETCH_SEED = 20261202
+
+
+def sketch_matrix(d_model: int) -> np.ndarray:
+    """[d_model, SKETCH_DIM] standard normal directions (a fixed seeded draw, test infrastructure)."""
+    return np.random.Generator(np.random.PCG64(SKETCH_SEED)).standard_normal((d_model, SKETCH_DIM))
+
+
+def row_sketch(rows: np.ndarray, r: np.ndarray) -> tuple:
+    """Per row of [..., D]: its Euclidean norm and its projection on the columns of r."""
+    return np.sqrt(np.sum(rows * rows, axis=-1)), rows @ r
 
 
 def input_digest(acts, w0) -> str:
@@ -57,10 +73,16 @@ def main(path: str) -> None:
     out = ob.stack_forward(ob.widen_bf16(acts["x"]), ob.widen_bf16(acts["txt"]), acts["txt_len"],
                            ob.widen_bf16(acts["cond"]), blocks(), cos, sin, geom.eps)
     rows = np.asarray(SAMPLE_ROWS, dtype=np.int64)
+    h0 = ob.join_rows(ob.widen_bf16(acts["x"]), ob.widen_bf16(acts["txt"]), acts["txt_len"])
+    r = sketch_matrix(geom.d_model)
+    n_out, p_out = row_sketch(out, r)
+    n_upd, p_upd = row_sketch(out - h0, r)
     np.savez_compressed(
         path,
         rows=rows,
         values=out[:, rows, :].astype(np.float32),
+        norm_out=n_out, proj_out=p_out.astype(np.float32), norm_upd=n_upd, proj_upd=p_upd.astype(np.float32),
+        max_abs=np.max(np.abs(out), axis=(1, 2)), max_abs_upd=np.max(np.abs(out - h0), axis=(1, 2)),
         item_rms=np.sqrt(np.mean(out * out, axis=(1, 2))),
         input_sha256=np.array(digest),
         n_blocks=np.array(geom.n_blocks),
