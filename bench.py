@@ -513,6 +513,22 @@ def stack_timing(torch, moss, geom, seed, reps=3):
     ms = e0.elapsed_time(e1) / reps
     tflop = geom.n_blocks * geom.block_flops() / 1e12
 
+    # the guidance pass with block 22 skipped on one branch (the CUDA port page, "What this changes"):
+    # the block runs on item 0's rows alone
+    skip = [[False, i == 22] for i in range(geom.n_blocks)]
+
+    def call_skip():
+        moss.moss_stack_forward_skip(dims, blocks, skip, x, txt, acts["txt_len"], cond, rope, out, ws)
+
+    call_skip()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        call_skip()
+    e1.record()
+    torch.cuda.synchronize()
+    skip_ms = e0.elapsed_time(e1) / reps
+
     # the whole denoiser forward around the same stack: timestep MLP, prompt and latent projections,
     # the 24 blocks, final norm and velocity projection
     enc_dim = synth.ENC_DIM
@@ -539,6 +555,7 @@ def stack_timing(torch, moss, geom, seed, reps=3):
     torch.cuda.empty_cache()
     return {"workload": "24-block stack, guidance pair: 2 items x (4096 image + 34 text rows; 34 and 10 valid)",
             "ms_per_call": round(ms, 3), "tflops": round(tflop / ms * 1e3, 1), "tflop_per_call": round(tflop, 2),
+            "ms_per_call_block22_skipped_by_item1": round(skip_ms, 3),
             "calls_timed": reps, "denoiser_forward_ms": round(den_ms, 3),
             "denoiser_forward_note": "the same stack with the ends: timestep MLP, prompt (4096-wide) and latent "
                                      "(128-wide) projections, final norm and velocity projection"}

@@ -183,7 +183,7 @@ struct FirstRows {
 };
 
 // mod: this block's modulation [B][6 D] (computed for the whole stack up front; items a block skips
-// have zero gates there, so the block leaves their residual unchanged).
+// have zero gates there, so a block run on them leaves their residual unchanged).
 int run_block(const Ctx& c, const moss_block_weights* w, const float* rope, float* h, uint16_t* out16,
               const float* mod, const FirstRows* first) {
   const moss_dims* d = c.d;
@@ -323,11 +323,52 @@ int run_stack(const Ctx& c, int n_blocks, const uint16_t* x, const uint16_t* txt
                "adaln_gemv");
     }
   }
+  const size_t item_elems = (size_t)(d->n_txt + d->n_img) * d->d_model;
   for (int i = 0; i < n_blocks; ++i) {
     const FirstRows rows{x, txt};
-    const int rc = run_block(c, &blocks[i], rope, h, i + 1 == n_blocks ? out : nullptr, mod + i * mod_stride,
-                             i == 0 ? &rows : nullptr);
-    if (rc != MOSS_OK) return rc;
+    uint16_t* out16 = i + 1 == n_blocks ? out : nullptr;
+    // the items this block runs on: all, a contiguous run [b0, b1) (the others skip it), or another
+    // pattern, which runs every item with the skipped items' gates zeroed (their residual passes
+    // through exactly; the modulation launch above zeroed them)
+    int b0 = 0, b1 = d->batch;
+    bool contiguous = true;
+    if (skip) {
+      const uint8_t* sk = skip + (size_t)i * d->batch;
+      b0 = 0;
+      while (b0 < d->batch && sk[b0]) ++b0;
+      b1 = b0;
+      while (b1 < d->batch && !sk[b1]) ++b1;
+      for (int b = b1; b < d->batch; ++b)
+        if (!sk[b]) contiguous = false;
+      if (!contiguous) b0 = 0, b1 = d->batch;
+    }
+    if (b0 == 0 && b1 == d->batch) {
+      const int rc = run_block(c, &blocks[i], rope, h, out16, mod + i * mod_stride, i == 0 ? &rows : nullptr);
+      if (rc != MOSS_OK) return rc;
+      continue;
+    }
+    // a block skipped by some items runs on the others' rows only
+    if (i == 0) {
+      StepTimer t(MOSS_STEP_JOIN, c.st);  // join every item's rows (the skipped ones keep them as they are)
+      MOSS_TRY(launch_join_rows(x, txt, c.lens, h, d->batch, d->n_txt, d->n_img, d->d_model, c.st), "join_rows");
+    }
+    if (b1 > b0) {
+      moss_dims sub = *d;
+      sub.batch = b1 - b0;
+      Ctx cs = c;
+      cs.d = &sub;
+      for (int b = 0; b < sub.batch; ++b) cs.lens.len[b] = c.lens.len[b0 + b];
+      const int rc = run_block(cs, &blocks[i], rope, h + b0 * item_elems, out16 ? out16 + b0 * item_elems : nullptr,
+                               mod + i * mod_stride + (size_t)b0 * 6 * d->d_model, nullptr);
+      if (rc != MOSS_OK) return rc;
+    }
+    if (out16) {
+      // the call's output for the items that skip its last block: their residual, rounded
+      for (int b = 0; b < d->batch; ++b)
+        if (b < b0 || b >= b1)
+          MOSS_TRY(launch_round_bf16(h + b * item_elems, out16 + b * item_elems, (int)item_elems, c.st),
+                   "round residual");
+    }
   }
   return MOSS_OK;
 }

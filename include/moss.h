@@ -167,11 +167,14 @@ int moss_stack_forward(const moss_dims* dims, int32_t n_blocks, const uint16_t* 
  * host array [n_blocks][batch] (row i for block i); a nonzero skip[i][b]
  * leaves item b's residual unchanged through block i while the other items
  * run it (the CUDA port page's guidance pass skips one block on one branch,
- * TensorFold PR #2281, "What this changes").  Implemented by zeroing that
- * item's two gates for that block, so its residual passes through exactly;
- * the block's compute is still spent on the item.  skip == NULL is
- * moss_stack_forward.  Other arguments, ownership and errors as
- * moss_stack_forward. */
+ * TensorFold PR #2281, "What this changes").  When the items that run a
+ * block are a contiguous run (in a guidance pair, always), the block runs on
+ * their rows alone and costs nothing for the others; a block no item runs
+ * launches nothing; other patterns run every item with the skipping items'
+ * two gates zeroed, so their residual still passes through exactly.  An item
+ * that skips the last block gets its residual, rounded to bf16, in `out`.
+ * skip == NULL is moss_stack_forward.  Other arguments, ownership and errors
+ * as moss_stack_forward. */
 int moss_stack_forward_skip(const moss_dims* dims, int32_t n_blocks, const uint16_t* x, const uint16_t* txt,
                             const int32_t* txt_len, const uint16_t* cond, const moss_block_weights* blocks,
                             const uint8_t* skip, const float* rope, uint16_t* out, void* workspace,

@@ -142,3 +142,54 @@ def test_stack_skip_35_blocks():
         G.assert_parity(f"out ({name} skips)", got, ref)
         res[name] = (got, ref)
     G.assert_parity("out(late) - out(early)", res["late"][0] - res["early"][0], res["late"][1] - res["early"][1])
+
+
+@pytest.mark.parametrize("batch,lens,skip", [
+    # item 0 skips the first block (the rows are joined for both, block 0 runs on item 1 alone), item 1
+    # skips block 1, item 0 skips the last block (its output is its residual, rounded)
+    (2, (8, 2), [[True, False], [False, True], [True, False]]),
+    # a block skipped by both items, then the last block skipped by item 1
+    (2, (8, 5), [[False, False], [True, True], [False, True]]),
+    # three items: a contiguous run in the middle (items 1 and 2 run block 0), then a pattern with a
+    # gap (items 0 and 2 run block 1: every item runs with item 1's gates zeroed)
+    (3, (8, 3, 6), [[True, False, False], [False, True, False], [False, False, True]]),
+])
+def test_stack_skip_runs_only_the_items_that_use_a_block(batch, lens, skip):
+    """Blocks skipped by some items run on the other items' rows only, against the oracle's per-item
+    stacks; an item's output through blocks it skips keeps its rows exactly."""
+    geom = synth.smaller(synth.CONFIGS["c0"], batch=batch, txt_len=lens)
+    G.say(f"stack_skip sub-batch runs B={batch} skip={skip}")
+    acts = synth.make_activations(geom, 16)
+    ws = [synth.make_block_weights(geom, 16, i, std=STRONG) for i in range(len(skip))]
+    got = G.host_f64(_stack_skip_gpu(geom, acts, ws, skip))
+    cos, sin = ob.rope_tables(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, geom.head_dim)
+    x, txt, cond = ob.widen_bf16(acts["x"]), ob.widen_bf16(acts["txt"]), ob.widen_bf16(acts["cond"])
+    ref = osm.stack_forward_skip(x, txt, acts["txt_len"], cond, [ob.weights_f64(w) for w in ws], skip, cos, sin,
+                                 geom.eps)
+    for b in range(batch):
+        h0 = ob.join_rows(x[b:b + 1], txt[b:b + 1], acts["txt_len"][b:b + 1])[0]
+        G.assert_parity(f"item {b} out", got[b], ref[b])
+        if all(s[b] for s in skip):
+            np.testing.assert_array_equal(got[b], h0)
+        else:
+            G.assert_parity(f"item {b} out - h0", got[b] - h0, ref[b] - h0)
+
+
+def test_stack_skip_guidance_pair_block_skipped_by_one_item():
+    """Two blocks at the full guidance-pair geometry (4096+34 rows, 34 and 10 text rows), the second
+    skipped by item 1: item 0 meets the bar against the two-block oracle, item 1 against one block."""
+    geom = synth.smaller(synth.CONFIGS["c4"], n_blocks=2)
+    G.say("stack_skip c4 x2, block 1 skipped by item 1")
+    acts = synth.make_activations(geom, 0)
+    ws = [synth.make_block_weights(geom, 0, i) for i in range(2)]
+    skip = [[False, False], [False, True]]
+    got = G.host_f64(_stack_skip_gpu(geom, acts, ws, skip))
+    cos, sin = ob.rope_tables(geom.n_txt, geom.grid_h, geom.grid_w, geom.theta, geom.head_dim)
+    x, txt, cond = ob.widen_bf16(acts["x"]), ob.widen_bf16(acts["txt"]), ob.widen_bf16(acts["cond"])
+    G.say("  oracle ...")
+    ref = osm.stack_forward_skip(x, txt, acts["txt_len"], cond, [ob.weights_f64(w) for w in ws], skip, cos, sin,
+                                 geom.eps)
+    h0 = ob.join_rows(x, txt, acts["txt_len"])
+    for b in range(2):
+        G.assert_parity(f"item {b} out", got[b], ref[b])
+        G.assert_parity(f"item {b} out - h0", got[b] - h0[b], ref[b] - h0[b])
