@@ -363,17 +363,25 @@ def step_work(geom):
     }
 
 
+def read_flush(torch):
+    """A 512 MB buffer whose sum, taken before a forward, leaves the 256 MB Infinity Cache holding
+    clean lines of that buffer: the forward's weights then come from HBM, and it does not also pay
+    for writing back a flush's dirty lines (a 512 MB fill does that)."""
+    buf = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+    return lambda: buf.sum()
+
+
 def per_step(torch, moss, step, geom, reps=5, cold=False):
     """Average launch time of each step inside block forwards (the library's probe), with the
-    Infinity Cache flushed before each forward when cold (a 512 MB fill between forwards)."""
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if cold else None
+    Infinity Cache flushed by a 512 MB read before each forward when cold."""
+    flush = read_flush(torch) if cold else None
     work = step_work(geom)
     res = {}
     for name in PROBED:
         moss.moss_probe_arm(name, reps)
         for _ in range(reps):
             if flush is not None:
-                flush.fill_(1)
+                flush()
             step()
         torch.cuda.synchronize()
         ms = moss.moss_probe_collect(reps)
@@ -393,6 +401,57 @@ def per_step(torch, moss, step, geom, reps=5, cold=False):
         elif mb:
             entry["hbm_frac"] = round(mb / us * 1e3 / PEAK_HBM_GBS, 4)
         res[name.lower()] = entry
+    return res
+
+
+def hbm_reference(torch, moss, geom, reps=15):
+    """The block's modulation GEMV and modulated RMSNorm, each alone (through its single-step entry
+    point), beside a torch kernel that moves the same bytes: a read-only sum of W_mod, a fp32 ->
+    bf16 conversion copy of h.  Each is timed between events on the stream right after a 512 MB
+    read flush (so the operands come from HBM), median of `reps`."""
+    d, m = geom.d_model, geom.batch * geom.rows
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    cond = torch.randn(geom.batch, d, generator=g, device="cuda").to(torch.bfloat16)
+    w_mod = (torch.randn(6 * d, d, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    mod = torch.empty(geom.batch, 6 * d, dtype=torch.float32, device="cuda")
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    h = torch.randn(m, d, generator=g, device="cuda")
+    shift, scale = mod[:, :d], mod[:, d:2 * d]
+    out16 = torch.empty(m, d, dtype=torch.bfloat16, device="cuda")
+    red = torch.empty((), dtype=torch.float32, device="cuda")
+    flush = read_flush(torch)
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            flush()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(1000.0 * a.elapsed_time(b))
+        return float(np.median(ts))
+
+    res = {}
+    gemv_mb, norm_mb = 2 * 6 * d * d / 1e6, 6 * m * d / 1e6
+    for name, ours, ref, mb, what in (
+            ("adaln_gemv", lambda: moss.moss_k_adaln_gemv(geom.batch, d, cond, w_mod, mod, ws),
+             lambda: torch.sum(w_mod, dim=(0, 1), dtype=torch.float32, out=red), gemv_mb,
+             "torch sum of W_mod (reads the same bytes)"),
+            ("mod_rmsnorm", lambda: moss.moss_k_mod_rmsnorm(geom.batch, geom.rows, d, geom.eps, h, shift, scale,
+                                                            6 * d, out16),
+             lambda: out16.copy_(h), norm_mb, "torch fp32 -> bf16 copy of h (reads and writes the same bytes)")):
+        for _ in range(3):
+            ours()
+            ref()
+        t_ours, t_ref = timed(ours), timed(ref)
+        res[name] = {"us": round(t_ours, 2), "hbm_frac": round(mb / t_ours * 1e3 / PEAK_HBM_GBS, 4),
+                     "same_bytes_us": round(t_ref, 2), "same_bytes_hbm_frac": round(mb / t_ref * 1e3 / PEAK_HBM_GBS, 4),
+                     "same_bytes_kernel": what}
+    del w_mod, h, out16
+    torch.cuda.empty_cache()
     return res
 
 
@@ -703,6 +762,7 @@ def main():
         print("bench: per-step times, 24-block stack, larger pictures", file=sys.stderr, flush=True)
         extras["step_times"] = per_step(torch, moss, step, geom)
         extras["step_times_cold_cache"] = per_step(torch, moss, step, geom, cold=True)
+        extras["hbm_reference"] = hbm_reference(torch, moss, geom)
         extras["stack_c4"] = stack_timing(torch, moss, synth.CONFIGS["c4"], args.seed)
         extras["larger_pictures"] = larger_pictures(torch, moss, w, args.seed)
 
