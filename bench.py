@@ -58,8 +58,8 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 CALIB_BYTES = 256 << 20  # the plain device copy the counters are scaled by
 PROBE_EVERY = 5  # the timed steps whose up projection the probe brackets: 0, 5, 10, ...
-# the up projection with the SiLU gate epilogue: whole 256-row tiles, then the 34 leftover rows as 64 x 128 tiles
-UP_KERNELS = ("gemm_nt_kernel<256, 256, 2, 4, 1>", "gemm_nt_kernel<64, 128, 2, 2, 1>")
+# the up projection with the SiLU gate epilogue: whole 256-row tiles, then the 34 leftover rows as 64 x 64 tiles
+UP_KERNELS = ("gemm_nt_kernel<256, 256, 2, 4, 1>", "gemm_nt_kernel<64, 64, 2, 1, 1>")
 GEMM_SOURCES = ("diffusion_transformer_denoiser_amd/csrc/gemm.hip", "diffusion_transformer_denoiser_amd/csrc/common.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_up_c2_traffic.md")
 METRIC = "denoiser block-forwards/s and TFLOP/s at 4096+34 tokens; MFMA % of peak"
@@ -136,7 +136,7 @@ def traffic_summary(fetch_dir, write_dir, geom):
     for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = read_counter_csv(folder, counter)
         # the up projection's dispatches (its two kernels run nowhere else in a block forward): the
-        # whole 256-row tiles, one workgroup per CU, then the 192 tail tiles of 64 x 128
+        # whole 256-row tiles, one workgroup per CU, then the 384 tail tiles of 64 x 64
         parts = [[v for name, grid, v in rows if kname in name] for kname in UP_KERNELS]
         copies = [v for name, _, v in rows if "copyBuffer" in name]
         if not parts[0] or not copies:
@@ -808,7 +808,7 @@ def main():
                                "MLP inner 12288 SiLU-gated, batch 1",
                    "global_batch": 1, "seq_len": geom.rows, "parallelism": "single GPU"},
         "roofline": {"kernel": f"up projection GEMM with the SiLU gate epilogue ({m} x {2 * geom.mlp_inner} x "
-                               f"{geom.d_model}; whole 256-row tiles, then the leftover rows as 64 x 128 tiles in a "
+                               f"{geom.d_model}; whole 256-row tiles, then the leftover rows as 64 x 64 tiles in a "
                                "second launch, timed together)",
                      "bound": "mfma",
                      "achieved": round(up_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -602,13 +602,18 @@ hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_
     hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI>), dim3(std::min(((m_main + 255) / 256) * nt, cus)),
                        dim3(512), 0, st, a, lda, w, ldw, c, ldc, 0, m_main, n, k, ep);
     if (split) {
-      // 64 x 128 tiles: twice the workgroups of 64 x 256 ones, so twice the CUs stream the weight
-      // panels (the tail is bound by reading all of w once): 50 -> 36 us for the 4096+34-row up
-      // projection
-      if (rem <= 64)
-        hipLaunchKernelGGL((gemm_nt_kernel<64, 128, 2, 2, EPI>), dim3(2 * nt), dim3(256), 0, st, a, lda, w, ldw, c,
-                           ldc, m_main, m, n, k, ep);
-      else
+      // The tail is bound by reading all of w once, so more workgroups stream it faster: 64 x 128
+      // tiles (twice the workgroups of 64 x 256) took the 4096+34-row up projection's tail from 50
+      // to 36 us, 64 x 64 tiles of two wavefronts (four times) 39-43 -> 37 us (same box).  The
+      // QKV epilogue needs a head's 128 columns in one pair of wavefronts, so it keeps 64 x 128.
+      if (rem <= 64) {
+        if constexpr (EPI != kQkvPack)
+          hipLaunchKernelGGL((gemm_nt_kernel<64, 64, 2, 1, EPI>), dim3(4 * nt), dim3(128), 0, st, a, lda, w, ldw, c,
+                             ldc, m_main, m, n, k, ep);
+        else
+          hipLaunchKernelGGL((gemm_nt_kernel<64, 128, 2, 2, EPI>), dim3(2 * nt), dim3(256), 0, st, a, lda, w, ldw, c,
+                             ldc, m_main, m, n, k, ep);
+      } else
         hipLaunchKernelGGL((gemm_nt_kernel<128, 128, 2, 2, EPI>), dim3(2 * nt), dim3(256), 0, st, a, lda, w, ldw, c,
                            ldc, m_main, m, n, k, ep);
     }
