@@ -8,7 +8,8 @@
 // the whole K loop.
 //
 //  * K advances 64 at a time through two LDS stages (128 KiB for the 256 x 256
-//    tiles).  Each slab is fetched straight into LDS with buffer_load_dwordx4
+//    tiles; launches whose tiles leave room, each workgroup waiting on its
+//    own loads, use three or four).  Each slab is fetched straight into LDS with buffer_load_dwordx4
 //    ... lds (issued from asm, see dma16_buf), the next slab's loads spread
 //    evenly over the MFMAs of the current slab's first two k16 steps, so they
 //    have the last two steps to land before the slab's one barrier.  A slab
@@ -358,7 +359,7 @@ __device__ __forceinline__ void epilogue_qkv(const f32x16 (&acc)[BN / WN / 32][B
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int EPI, int NST = 2>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __restrict__ a, int lda,
                                                              const uint16_t* __restrict__ w, int ldw,
                                                              uint16_t* __restrict__ c, int ldc, int m_begin,
@@ -375,7 +376,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
   constexpr int PER = LA + LB;
   static_assert(CA * 1024 == AB && LB * NW * 1024 == BB, "slab / wavefront mismatch");
   static_assert(EPI != kSiluGate || FN % 2 == 0, "the SiLU epilogue pairs gate and up fragments per wavefront");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * SB];
+  static_assert(NST >= 2 && (NST - 2) * PER <= 63, "stages, and the loads a slab wait leaves in flight");
+  __shared__ __attribute__((aligned(1024))) char smem[NST * SB];
 
   // This launch covers rows [m_begin, m).  Workgroup b computes tiles b, b + G, b + 2G, ... of the
   // launch (G workgroups); the loads run on from one of its tiles into the next, so a tile's first
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
     else
       dma16_buf(vb[q - LA] + lk * (KB * 2), rw, base + AB + 1024u * (wv + NW * (q - LA)));
     if (q == PER - 1) {
-      lst ^= 1;
+      lst = lst + 1 == NST ? 0 : lst + 1;
       if (++lk == nk) {
         lk = 0;
         if (++lt < mine) aim(lt);
@@ -465,11 +467,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
       fa[x - FN] = *reinterpret_cast<const bf16x8*>(st + offa[s][x - FN]);
   };
 
+  // the first NST - 1 slabs; then wait for slab 0 alone
   aim(0);
-  if (total > 0)
 #pragma unroll
-    for (int q = 0; q < PER; ++q) issue_one(q);
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  for (int sl = 0; sl < NST - 1; ++sl)
+    if (sl < total)
+#pragma unroll
+      for (int q = 0; q < PER; ++q) issue_one(q);
+  if (NST > 2 && total >= NST - 1)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NST - 2) * PER) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
   int g = 0;  // the slab being consumed, counted over this workgroup's tiles
   for (int r = 0; r < mine; ++r) {
@@ -486,8 +494,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     for (int kt = 0; kt < nk; ++kt, ++g) {
-      const char* cur = smem + (g & 1) * SB;
-      const bool more = g + 1 < total;  // slab g + 1 is loaded into the other stage during steps 0-1
+      const char* cur = smem + (g % NST) * SB;
+      const bool more = g + NST - 1 < total;  // slab g + NST - 1 is loaded during steps 0-1
       bf16x8 fa[2][FM], fw[2][FN];
 #pragma unroll
       for (int x = 0; x < NR; ++x) rd(cur, 0, x, fa[0], fw[0]);
@@ -514,15 +522,20 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // slab g + 1 resident and every read of slab g done before the next slab's loads overwrite it
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      // slab g + 1 resident and every read of slab g done before the next slab's loads overwrite it.
+      // Loads complete in order, so leaving the newest (NST - 2) * PER (the slabs after g + 1) in
+      // flight is exact; epilogue stores issued in between only make the wait longer.
+      if (NST > 2 && g + NST - 1 < total)
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NST - 2) * PER) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     }
 
     if constexpr (EPI == kQkvPack) {
-      // the stage of the tile's last slab stays free until the next tile's second slab is loaded
-      char* spare = smem + ((g + 1) & 1) * SB;
+      // the stage of the tile's last slab stays free until the next tile's slab NST - 1 is loaded
+      char* spare = smem + ((g + NST - 1) % NST) * SB;
       epilogue_qkv<BM, BN, WM, WN>(acc, spare, m0, n0, wave, wm, wn, l32, hh, m, ep);
-    } else if constexpr (EPI == kGatedAdd && WM == 1 && WN == 8 && BN == 256) {
+    } else if constexpr (EPI == kGatedAdd && WM == 1 && WN == 8 && BN == 256 && NST == 2) {
       if (r + 1 == mine)
         epilogue_gated_lds<BM, BN, WM, WN>(acc, smem, m0, n0, wave, l32, hh, m, n, ep);
       else
@@ -578,7 +591,9 @@ hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_
                            lda, w, ldw, c, ldc, 0, m, nt1 * 256, k, ep);
         EpiArgs ep2 = ep;
         ep2.col0 = ep.col0 + nt1 * 256;
-        hipLaunchKernelGGL((gemm_nt_kernel<128, 256, 2, 4, EPI>), dim3(mt2 * nt2), dim3(512), 0, st, a, lda,
+        // three stages (144 KiB): one workgroup per tile, each waiting on its loads; a third stage
+        // keeps two slabs in flight (QKV's six column tiles at 4130 rows: 55 -> 47 us, same box)
+        hipLaunchKernelGGL((gemm_nt_kernel<128, 256, 2, 4, EPI, 3>), dim3(mt2 * nt2), dim3(512), 0, st, a, lda,
                            w + (size_t)nt1 * 256 * ldw, ldw, c ? c + (size_t)nt1 * 256 : c, ldc, 0, m, nt2 * 256, k,
                            ep2);
         return hipGetLastError();
@@ -602,20 +617,21 @@ hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_
     hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI>), dim3(std::min(((m_main + 255) / 256) * nt, cus)),
                        dim3(512), 0, st, a, lda, w, ldw, c, ldc, 0, m_main, n, k, ep);
     if (split) {
-      // The tail is bound by reading all of w once, so more workgroups stream it faster: 64 x 128
-      // tiles (twice the workgroups of 64 x 256) took the 4096+34-row up projection's tail from 50
-      // to 36 us, 64 x 64 tiles of two wavefronts (four times) 39-43 -> 37 us (same box).  The
-      // QKV epilogue needs a head's 128 columns in one pair of wavefronts, so it keeps 64 x 128.
+      // The tail is bound by reading all of w once: more workgroups, and more slabs in flight per
+      // workgroup, stream it faster.  At the 4096+34-row up projection: 64 x 128 tiles (twice the
+      // workgroups of 64 x 256) 50 -> 36 us; 64 x 64 tiles of two wavefronts (four times) 39-43 ->
+      // 37 us; their ring at four stages instead of two 37 -> 27 us (same box).  The QKV epilogue
+      // needs a head's 128 columns in one pair of wavefronts, so it keeps 64 x 128.
       if (rem <= 64) {
         if constexpr (EPI != kQkvPack)
-          hipLaunchKernelGGL((gemm_nt_kernel<64, 64, 2, 1, EPI>), dim3(4 * nt), dim3(128), 0, st, a, lda, w, ldw, c,
-                             ldc, m_main, m, n, k, ep);
+          hipLaunchKernelGGL((gemm_nt_kernel<64, 64, 2, 1, EPI, 4>), dim3(4 * nt), dim3(128), 0, st, a, lda, w, ldw,
+                             c, ldc, m_main, m, n, k, ep);
         else
-          hipLaunchKernelGGL((gemm_nt_kernel<64, 128, 2, 2, EPI>), dim3(2 * nt), dim3(256), 0, st, a, lda, w, ldw, c,
-                             ldc, m_main, m, n, k, ep);
+          hipLaunchKernelGGL((gemm_nt_kernel<64, 128, 2, 2, EPI, 4>), dim3(2 * nt), dim3(256), 0, st, a, lda, w, ldw,
+                             c, ldc, m_main, m, n, k, ep);
       } else
-        hipLaunchKernelGGL((gemm_nt_kernel<128, 128, 2, 2, EPI>), dim3(2 * nt), dim3(256), 0, st, a, lda, w, ldw, c,
-                           ldc, m_main, m, n, k, ep);
+        hipLaunchKernelGGL((gemm_nt_kernel<128, 128, 2, 2, EPI, 3>), dim3(2 * nt), dim3(256), 0, st, a, lda, w, ldw,
+                           c, ldc, m_main, m, n, k, ep);
     }
   } else {
     hipLaunchKernelGGL((gemm_nt_kernel<256, 128, 4, 2, EPI>), dim3(((m + 255) / 256) * (n / 128)), dim3(512), 0, st,
