@@ -23,8 +23,8 @@
 //  * The 16-byte chunk c of row r is stored at c ^ ((r >> 1) & 7), so the 16
 //    rows a 16-lane group reads for one operand fragment land in 16 distinct
 //    16-byte slots of the LDS banks.
-//  * Tiles are numbered in groups of six column tiles, row-major within a
-//    group, and workgroup ids (dealt round-robin over the 8 XCDs) are
+//  * Tiles are numbered in groups of six column tiles (sixteen for the up
+//    projection), row-major within a group, and workgroup ids (dealt round-robin over the 8 XCDs) are
 //    remapped so each XCD runs a contiguous stretch of that order: the ~32
 //    tiles an XCD holds at once span about 5 row and 6 column panels, which
 //    its L2 shares (fetch from beyond L2 down ~40% from an M-fastest order).
@@ -79,21 +79,29 @@ struct EpiArgs {
   int col0;           // kQkvPack: absolute column of this launch's column 0
 };
 
-constexpr int kGroupN = 6;  // column tiles per group of the tile order
+// Column tiles per group of the tile order.  The up projection's whole tiles (96 column tiles)
+// take groups of 16: 4 us faster than 6 over two interleaved same-box runs (12: the same, 24 and
+// 48 slower); QKV's and the out and down projections' sweeps (3, 4, 10, 12, 15) stayed within
+// the runs' 1% spread, so they keep 6.
+constexpr int kGroupN = 6;
+constexpr int kGroupNUp = 16;
+constexpr int kGroupNQkv = 6;
+constexpr int kGroupNGated = 6;
 
 // Workgroup id -> (tile_m, tile_n).  Logical order: column tiles in groups of
-// kGroupN, each group row-major (N fastest); workgroup ids are dealt
-// round-robin over the 8 XCDs, so they are remapped to give each XCD a
-// contiguous run of that order.
+// GRP, each group row-major (N fastest); workgroup ids are dealt round-robin
+// over the 8 XCDs, so they are remapped to give each XCD a contiguous run of
+// that order.
+template <int GRP>
 __device__ __forceinline__ void tile_of(int id, int mt, int nt, int& tm, int& tn) {
   const int nblk = mt * nt;
   const int per = nblk / 8, rem = nblk % 8;
   const int x = id % 8, l = id / 8;
   const int logical = (x < rem) ? x * (per + 1) + l : rem * (per + 1) + (x - rem) * per + l;
-  const int g = logical / (kGroupN * mt), r = logical % (kGroupN * mt);
-  const int cols = min(kGroupN, nt - g * kGroupN);
+  const int g = logical / (GRP * mt), r = logical % (GRP * mt);
+  const int cols = min(GRP, nt - g * GRP);
   tm = r / cols;
-  tn = g * kGroupN + r % cols;
+  tn = g * GRP + r % cols;
 }
 
 // acc[i][j] is a 32 x 32 tile of c^T: lane holds row m = l32 of c and
@@ -359,7 +367,7 @@ __device__ __forceinline__ void epilogue_qkv(const f32x16 (&acc)[BN / WN / 32][B
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int NST = 2>
+template <int BM, int BN, int WM, int WN, int EPI, int NST = 2, int GRP = kGroupN>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __restrict__ a, int lda,
                                                              const uint16_t* __restrict__ w, int ldw,
                                                              uint16_t* __restrict__ c, int ldc, int m_begin,
@@ -402,7 +410,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
   uint32_t va[LA], vb[LB];  // byte offsets of this lane's 16 bytes of slab 0 of the current tile
   auto aim = [&](int r) {    // point the loads at this workgroup's tile r
     int tm, tn;
-    tile_of(blockIdx.x + r * G, mt, ntn, tm, tn);
+    tile_of<GRP>(blockIdx.x + r * G, mt, ntn, tm, tn);
     const int m0 = m_begin + tm * BM, n0 = tn * BN;
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
@@ -482,7 +490,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
   int g = 0;  // the slab being consumed, counted over this workgroup's tiles
   for (int r = 0; r < mine; ++r) {
     int tm, tn;
-    tile_of(blockIdx.x + r * G, mt, ntn, tm, tn);
+    tile_of<GRP>(blockIdx.x + r * G, mt, ntn, tm, tn);
     const int m0 = m_begin + tm * BM, n0 = tn * BN;
 
     f32x16 acc[FN][FM];
@@ -587,7 +595,7 @@ hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_
       const int mt = (m + 255) / 256, rounds = mt * nt / cus, left = mt * nt % cus;
       const int nt1 = rounds * cus / mt, nt2 = nt - nt1, mt2 = (m + 127) / 128;
       if (rounds >= 1 && left > 0 && 2 * left <= cus && nt1 > 0 && nt2 > 0 && mt2 * nt2 <= cus) {
-        hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI>), dim3(std::min(mt * nt1, cus)), dim3(512), 0, st, a,
+        hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI, 2, kGroupNQkv>), dim3(std::min(mt * nt1, cus)), dim3(512), 0, st, a,
                            lda, w, ldw, c, ldc, 0, m, nt1 * 256, k, ep);
         EpiArgs ep2 = ep;
         ep2.col0 = ep.col0 + nt1 * 256;
@@ -608,13 +616,14 @@ hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_
       // 224 x 64 (1 per SIMD) kept less.
       const int t256 = ((m + 255) / 256) * nt, t224 = ((m + 223) / 224) * nt;
       if (!split && (t224 + cus - 1) / cus == (t256 + cus - 1) / cus) {
-        hipLaunchKernelGGL((gemm_nt_kernel<224, 256, 1, 8, EPI>), dim3(t224), dim3(512), 0, st, a, lda, w, ldw, c,
+        hipLaunchKernelGGL((gemm_nt_kernel<224, 256, 1, 8, EPI, 2, kGroupNGated>), dim3(t224), dim3(512), 0, st, a, lda, w, ldw, c,
                            ldc, 0, m, n, k, ep);
         return hipGetLastError();
       }
     }
     // one workgroup per CU, each taking every cus-th tile
-    hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI>), dim3(std::min(((m_main + 255) / 256) * nt, cus)),
+    constexpr int grp = EPI == kSiluGate ? kGroupNUp : kGroupN;
+    hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI, 2, grp>), dim3(std::min(((m_main + 255) / 256) * nt, cus)),
                        dim3(512), 0, st, a, lda, w, ldw, c, ldc, 0, m_main, n, k, ep);
     if (split) {
       // The tail is bound by reading all of w once: more workgroups, and more slabs in flight per
