@@ -313,16 +313,22 @@ __device__ __forceinline__ void epilogue_qkv(const f32x16 (&acc)[BN / WN / 32][B
         g[i][q][3] = bf16_hi(w2[1]);
       }
     uint16_t* dbase = which ? ep.ko : ep.qo;
+    // Each 32-row block's results go through this wavefront's 4 KiB of LDS (its own: no barrier)
+    // and leave as whole 128-byte half-head rows, eight rows per store instruction: stored straight
+    // from the MFMA layout, each instruction wrote 16 bytes into each of 64 rows, and the q/k
+    // stores cost about 15 us of the QKV projection.  Chunk c of row r sits at c ^ (r & 7).
+    static_assert(WM * WN * 4096 <= (BM + BN) * KB * 2, "the transposes fit one ring stage");
+    char* tr = smem + wave * 4096;
+    const int lane = l32 + 32 * hh;
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       const int row = m0 + wm * TM + j * 32 + l32;
-      if (row >= m) continue;
+      if (row < m) {
       const int b = row / T, t = row - b * T;
       const float r = 1.0f / sqrtf(ss[j] / 128.0f + ep.eps);
       // pairs p0 = half*32 + 16 i + 4 q + 2 hh and p0 + 1: one 16-byte entry of the pair-of-pairs table
       // per (i, q); the 32 lanes of a half wavefront read 32 consecutive rows of it, 512 contiguous bytes
       const float* cr = ep.rope_pp + ((size_t)(half * 16 + hh) * ep.rows_pad + t) * 4;
-      uint16_t* dst = dbase + (((size_t)b * H + head) * ep.rows_pad + t) * 128 + half * 64 + 8 * hh;
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -344,10 +350,28 @@ __device__ __forceinline__ void epilogue_qkv(const f32x16 (&acc)[BN / WN / 32][B
             }
             v[qq] = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
           }
-          // dims 8 (2p + hh) + (0..7) of this half head
-          *reinterpret_cast<u32x4*>(dst + i * 32 + 16 * p) = pair_cols(v[0], v[1]);
+          // dims 32 i + 8 (2p + hh) + (0..7) of this half head: chunk 4 i + 2 p + hh of the row
+          const int c = 4 * i + 2 * p + hh;
+          *reinterpret_cast<u32x4*>(tr + l32 * 128 + ((c ^ (l32 & 7)) * 16)) = pair_cols(v[0], v[1]);
         }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // lane: chunk lane & 7 of rows k*8 + lane/8 of the block
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int rr = 8 * k + (lane >> 3), cc = lane & 7;
+        const int row2 = m0 + wm * TM + j * 32 + rr;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(tr + rr * 128 + ((cc ^ (rr & 7)) * 16));
+        if (row2 < m) {
+          const int b2 = row2 / T, t2 = row2 - b2 * T;
+          *reinterpret_cast<u32x4*>(dbase + (((size_t)b2 * H + head) * ep.rows_pad + t2) * 128 + half * 64 + cc * 8) =
+              val;
+        }
+      }
     }
+    // every wavefront done with its transposes before any of them starts the next tile, whose slab
+    // loads go into this stage (all wavefronts of a tile take this branch: a tile lies in q, k or v)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   } else {
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
