@@ -8,14 +8,14 @@
 // the whole K loop.
 //
 //  * K advances 64 at a time through two LDS stages (128 KiB for the 256 x 256
-//    tiles; launches whose tiles leave room, each workgroup waiting on its
-//    own loads, use three or four).  Each slab is fetched straight into LDS with buffer_load_dwordx4
-//    ... lds (issued from asm, see dma16_buf), the next slab's loads spread
-//    evenly over the MFMAs of the current slab's first two k16 steps, so they
-//    have the last two steps to land before the slab's one barrier.  A slab
-//    row is 128 bytes: every load covers whole cache lines (32-k slabs read
-//    half lines, twice as many L2 requests; 4096 x 24576 x 3072 went from
-//    519 to 483 us standalone with this scheme).
+//    tiles; launches of one tile per workgroup whose tiles leave room use
+//    three or four).  Each slab is fetched straight into LDS with
+//    buffer_load_dwordx4 ... lds (issued from asm, see dma16_buf), the next
+//    slab's loads spread evenly over the MFMAs of the current slab's first
+//    two k16 steps, so they have the last two steps to land before the slab's
+//    one barrier.  A slab row is 128 bytes: every load covers whole cache
+//    lines (32-k slabs read half lines, twice as many L2 requests; 4096 x
+//    24576 x 3072 went from 519 to 483 us standalone with this scheme).
 //  * The MFMA operands of the next k16 step are read from LDS into registers
 //    during the current one, one read after each of its first MFMAs; nothing
 //    is reordered across those points (sched_barrier), so the reads, loads
@@ -24,10 +24,11 @@
 //    rows a 16-lane group reads for one operand fragment land in 16 distinct
 //    16-byte slots of the LDS banks.
 //  * Tiles are numbered in groups of six column tiles (sixteen for the up
-//    projection), row-major within a group, and workgroup ids (dealt round-robin over the 8 XCDs) are
-//    remapped so each XCD runs a contiguous stretch of that order: the ~32
-//    tiles an XCD holds at once span about 5 row and 6 column panels, which
-//    its L2 shares (fetch from beyond L2 down ~40% from an M-fastest order).
+//    projection), row-major within a group, and workgroup ids (dealt
+//    round-robin over the 8 XCDs) are remapped so each XCD runs a contiguous
+//    stretch of that order: with groups of six, the ~32 tiles an XCD holds at
+//    once span about 5 row and 6 column panels, which its L2 shares (fetch
+//    from beyond L2 down ~40% from an M-fastest order).
 //  * The weight tile is the MFMA's first operand and the activation tile the
 //    second, so a lane's accumulators hold runs of four consecutive output
 //    columns of one row; lane pairs trade halves (pair_cols) so that bf16
@@ -36,6 +37,8 @@
 //  * Launches with more tiles than CUs run one workgroup per CU, each taking
 //    every G-th tile in turn; its loads run on across its tiles, so a tile's
 //    first slab is in LDS when the previous tile's epilogue starts.
+//  * The QKV epilogue's q and k rows pass through LDS so that each store
+//    instruction writes whole 128-byte half-head rows.
 // There is no split-K and no atomic: results are identical call to call.
 //
 // Epilogues (the MOSS-Image transformer page's SiLU and gated-add kernels,
