@@ -28,7 +28,11 @@ oracle on block forwards of the same workload.
 After the main timing (unless ``--no-extras``) the line also carries: each
 step's launch time inside block forwards (the library's probe) with its
 fraction of the MFMA or HBM peak, warm and with the 256 MB Infinity Cache
-flushed before every forward; the 24-block guidance-pair stack (two items of
+flushed before every forward (``step_times_cold_cache``: a 512 MB fill, which
+also leaves dirty lines for the forward's reads to evict;
+``step_times_cold_read``: a 512 MB read, which does not); the modulation GEMV
+and the norm each alone beside a torch kernel moving the same bytes
+(``hbm_reference``); the 24-block guidance-pair stack (two items of
 4096 image + 34 text rows) in ms per call; the larger pictures (block and
 attention time against the square of the row count); and the block replayed
 from a captured HIP graph.
@@ -372,10 +376,17 @@ def read_flush(torch):
     return lambda: buf.sum()
 
 
-def per_step(torch, moss, step, geom, reps=5, cold=False):
-    """Average launch time of each step inside block forwards (the library's probe), with the
-    Infinity Cache flushed by a 512 MB read before each forward when cold."""
-    flush = read_flush(torch) if cold else None
+def write_flush(torch):
+    """A 512 MB fill before a forward (the cold-cache protocol as specified): it evicts the 256 MB
+    Infinity Cache, and leaves it full of dirty lines that the next kernels' reads evict."""
+    buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    return lambda: buf.fill_(1)
+
+
+def per_step(torch, moss, step, geom, reps=5, cold=None):
+    """Average launch time of each step inside block forwards (the library's probe); cold is None
+    (warm), "write" (a 512 MB fill before each forward) or "read" (a 512 MB read before each)."""
+    flush = {None: lambda t: None, "write": write_flush, "read": read_flush}[cold](torch)
     work = step_work(geom)
     res = {}
     for name in PROBED:
@@ -762,7 +773,8 @@ def main():
     if not args.no_extras:
         print("bench: per-step times, 24-block stack, larger pictures", file=sys.stderr, flush=True)
         extras["step_times"] = per_step(torch, moss, step, geom)
-        extras["step_times_cold_cache"] = per_step(torch, moss, step, geom, cold=True)
+        extras["step_times_cold_cache"] = per_step(torch, moss, step, geom, cold="write")
+        extras["step_times_cold_read"] = per_step(torch, moss, step, geom, cold="read")
         extras["hbm_reference"] = hbm_reference(torch, moss, geom)
         extras["stack_c4"] = stack_timing(torch, moss, synth.CONFIGS["c4"], args.seed)
         extras["larger_pictures"] = larger_pictures(torch, moss, w, args.seed)
