@@ -528,12 +528,20 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+    // Scalar loads (kernel arguments the epilogue uses) complete out of order, so while the
+    // compiler counts one as possibly in flight it makes every LDS wait a full lgkmcnt(0); waiting
+    // for them here, visibly, lets the k-loop's first MFMA wait for its own two fragments only.
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt and expcnt unconstrained
     for (int kt = 0; kt < nk; ++kt, ++g) {
       const char* cur = smem + (g % NST) * SB;
       const bool more = g + NST - 1 < total;  // slab g + NST - 1 is loaded during steps 0-1
       bf16x8 fa[2][FM], fw[2][FN];
 #pragma unroll
-      for (int x = 0; x < NR; ++x) rd(cur, 0, x, fa[0], fw[0]);
+      for (int x = 0; x < NR; ++x) {
+        // in use order, so the first MFMA waits for its own two fragments only
+        rd(cur, 0, x, fa[0], fw[0]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma clang loop unroll(full)
       for (int s = 0; s < 4; ++s) {
 #pragma clang loop unroll(full)
