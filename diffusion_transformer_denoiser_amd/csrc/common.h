@@ -114,6 +114,15 @@ __device__ __forceinline__ void dma16_buf(uint32_t voff, u32x4 rsrc, uint32_t ld
                : "memory");
 }
 
+// As dma16_buf, the byte offset split into a per-lane part (voff) and a wave-uniform part (soff,
+// the buffer instruction's scalar offset: no per-lane add).  The resource's bounds check covers voff
+// only, so the caller keeps voff + soff in bounds itself.
+__device__ __forceinline__ void dma16_buf_so(uint32_t voff, u32x4 rsrc, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(rsrc),
+               "s"(soff)
+               : "memory");
+}
+
 // Per-launch batch metadata passed by value (txt_len lives on the host).
 struct ItemLens {
   int32_t len[MOSS_MAX_BATCH];

@@ -461,11 +461,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
   const uint32_t lds0 = (uint32_t)(uintptr_t)(MOSS_LDS char*)smem;
   int lt = 0, lk = 0, lst = 0;  // the next slab to load: tile, slab within it, stage
   auto issue_one = [&](int q) {  // load instruction q of that slab; the last one moves on
-    const uint32_t base = lds0 + (uint32_t)(lst * SB);
+    const uint32_t base = lds0 + (uint32_t)(lst * SB), koff = (uint32_t)(lk * (KB * 2));
     if (q < LA)
-      dma16_buf(va[q] + lk * (KB * 2), ra, base + ca[q]);
+      dma16_buf_so(va[q], ra, koff, base + ca[q]);
     else
-      dma16_buf(vb[q - LA] + lk * (KB * 2), rw, base + AB + 1024u * (wv + NW * (q - LA)));
+      dma16_buf_so(vb[q - LA], rw, koff, base + AB + 1024u * (wv + NW * (q - LA)));
     if (q == PER - 1) {
       lst = lst + 1 == NST ? 0 : lst + 1;
       if (++lk == nk) {
@@ -533,8 +533,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
     // for them here, visibly, lets the k-loop's first MFMA wait for its own two fragments only.
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt and expcnt unconstrained
     for (int kt = 0; kt < nk; ++kt, ++g) {
+      // slab g + NST - 1 is loaded during steps 0-1.  Past a workgroup's last slab the loads go on
+      // without a test (no branch among the MFMAs): they read rows of its last tile again, in
+      // bounds, into the stage of a slab already consumed, and the last slab waits for them.
       const char* cur = smem + (g % NST) * SB;
-      const bool more = g + NST - 1 < total;  // slab g + NST - 1 is loaded during steps 0-1
       bf16x8 fa[2][FM], fw[2][FN];
 #pragma unroll
       for (int x = 0; x < NR; ++x) {
@@ -557,7 +559,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
             for (int x = t; x < (t + 1 == NMF ? NR : t + 1); ++x)
               if (x < NR) rd(cur, s + 1, x, fa[(s + 1) & 1], fw[(s + 1) & 1]);
           }
-          if (s < 2 && more) {
+          if (s < 2) {
             const int u = s * NMF + t;
 #pragma unroll
             for (int q = u * PER / (2 * NMF); q < (u + 1) * PER / (2 * NMF); ++q) issue_one(q);
