@@ -501,6 +501,28 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
     else
       fa[x - FN] = *reinterpret_cast<const bf16x8*>(st + offa[s][x - FN]);
   };
+  // The LDS addresses of k-step 0's reads of the next slab, worked out during the current slab's
+  // last k-step so that those reads issue straight after the slab barrier.
+  int stage = 0;  // g % NST
+  uint32_t nx[NR];
+  auto set_next = [&](int st) {
+#pragma unroll
+    for (int x = 0; x < NR; ++x)
+      nx[x] = lds0 + (uint32_t)(st * SB) +
+              (uint32_t)(x == 0 ? offb[0][0] : x == 1 ? offa[0][0] : x < FN + 1 ? offb[0][x - 1] : offa[0][x - FN]);
+  };
+  auto rd0 = [&](int x, bf16x8* fa, bf16x8* fw) {
+    const bf16x8 v = *reinterpret_cast<MOSS_LDS const bf16x8*>((size_t)nx[x]);
+    if (x == 0)
+      fw[0] = v;
+    else if (x == 1)
+      fa[0] = v;
+    else if (x < FN + 1)
+      fw[x - 1] = v;
+    else
+      fa[x - FN] = v;
+  };
+  set_next(0);
 
   // the first NST - 1 slabs; then wait for slab 0 alone
   aim(0);
@@ -536,12 +558,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
       // slab g + NST - 1 is loaded during steps 0-1.  Past a workgroup's last slab the loads go on
       // without a test (no branch among the MFMAs): they read rows of its last tile again, in
       // bounds, into the stage of a slab already consumed, and the last slab waits for them.
-      const char* cur = smem + (g % NST) * SB;
+      const char* cur = smem + stage * SB;
       bf16x8 fa[2][FM], fw[2][FN];
 #pragma unroll
       for (int x = 0; x < NR; ++x) {
         // in use order, so the first MFMA waits for its own two fragments only
-        rd(cur, 0, x, fa[0], fw[0]);
+        rd0(x, fa[0], fw[0]);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma clang loop unroll(full)
@@ -559,6 +581,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
             for (int x = t; x < (t + 1 == NMF ? NR : t + 1); ++x)
               if (x < NR) rd(cur, s + 1, x, fa[(s + 1) & 1], fw[(s + 1) & 1]);
           }
+          if (s == 3 && t == 0) set_next(stage + 1 == NST ? 0 : stage + 1);
           if (s < 2) {
             const int u = s * NMF + t;
 #pragma unroll
@@ -574,6 +597,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
         asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NST - 2) * PER) : "memory");
       else
         asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      stage = stage + 1 == NST ? 0 : stage + 1;
     }
 
     if constexpr (EPI == kQkvPack) {
