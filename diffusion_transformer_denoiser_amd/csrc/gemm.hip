@@ -52,6 +52,7 @@
 //    the fp32 residual, or, for the last add of a call, out = bf16(h + gate *
 //    acc) with h unchanged.  The projection output is never stored.
 #include <algorithm>
+#include <type_traits>
 #include <cmath>
 
 #include "common.h"
@@ -542,19 +543,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
     tile_of<GRP>(blockIdx.x + r * G, mt, ntn, tm, tn);
     const int m0 = m_begin + tm * BM, n0 = tn * BN;
 
+    // the tile's first k-step starts its sums from zero (the MFMAs take 0 as the accumulator input,
+    // so no registers are cleared per tile): the first slab is a separate copy of the slab body
     f32x16 acc[FN][FM];
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-      for (int j = 0; j < FM; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     // Scalar loads (kernel arguments the epilogue uses) complete out of order, so while the
     // compiler counts one as possibly in flight it makes every LDS wait a full lgkmcnt(0); waiting
     // for them here, visibly, lets the k-loop's first MFMA wait for its own two fragments only.
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt and expcnt unconstrained
-    for (int kt = 0; kt < nk; ++kt, ++g) {
+    auto slab = [&](auto first_slab) {
+      constexpr bool FIRST = decltype(first_slab)::value;
       // slab g + NST - 1 is loaded during steps 0-1.  Past a workgroup's last slab the loads go on
       // without a test (no branch among the MFMAs): they read rows of its last tile again, in
       // bounds, into the stage of a slab already consumed, and the last slab waits for them.
@@ -571,7 +569,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
 #pragma clang loop unroll(full)
         for (int t = 0; t < NMF; ++t) {
           const int j = t / FN, i = t % FN;
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[s & 1][i], fa[s & 1][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[s & 1][i], fa[s & 1][j],
+                                                              FIRST && s == 0 ? f32x16{} : acc[i][j], 0, 0, 0);
           // one fragment read of the next k-step after each of the first MFMAs (the rest after the
           // last one when there are more reads than MFMAs), and the next slab's loads spread evenly
           // over the MFMAs of k-steps 0 and 1; nothing moves across these points
@@ -598,7 +597,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
       else
         asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
       stage = stage + 1 == NST ? 0 : stage + 1;
-    }
+      ++g;
+    };
+    slab(std::true_type{});  // nk >= 1: the launcher refuses k < 64
+    for (int kt = 1; kt < nk; ++kt) slab(std::false_type{});
 
     if constexpr (EPI == kQkvPack) {
       // the stage of the tile's last slab stays free until the next tile's slab NST - 1 is loaded
@@ -637,7 +639,7 @@ template <int EPI>
 hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_t* w, int ldw, uint16_t* c, int ldc,
                   const EpiArgs& ep, hipStream_t st) {
   // the kernels address both operands through 32-bit buffer byte offsets
-  if ((size_t)m * lda * 2 > 0xffffffffu || (size_t)n * ldw * 2 > 0xffffffffu || k % KB != 0)
+  if ((size_t)m * lda * 2 > 0xffffffffu || (size_t)n * ldw * 2 > 0xffffffffu || k <= 0 || k % KB != 0)
     return hipErrorInvalidValue;
   if (n % 256 == 0) {
     const int nt = n / 256, full = m / 256, rem = m % 256, cus = cu_count();
