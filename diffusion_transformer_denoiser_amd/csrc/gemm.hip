@@ -475,45 +475,43 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
       }
     }
   };
-  // byte offsets of this lane's fragments within a stage, for the four k16 steps of a slab
-  int offa[4][FM], offb[4][FN];
+  // Byte offsets of this lane's fragments within a stage.  Fragment j of the A tile (i of the
+  // weight tile) covers rows wm*TM + 32j + l32 (wn*TN + 32i + l32); TM and TN are multiples of 16,
+  // so a row's chunk swizzle (row >> 1) & 7 is the lane's own, and fragment j sits 32 rows (4 KiB)
+  // past fragment 0: one base per k16 step, the 4 KiB steps folded into the reads' offset field.
+  static_assert(TM % 16 == 0 && TN % 16 == 0, "fragment blocks share the lane's swizzle");
+  constexpr uint32_t FRAG = 32 * KB * 2;  // bytes between consecutive 32-row fragment blocks
+  const int swz = (l32 >> 1) & 7;
+  uint32_t oa[4], ob[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int r = wm * TM + j * 32 + l32;
-      offa[s][j] = r * (KB * 2) + ((2 * s + hh) ^ ((r >> 1) & 7)) * 16;
-    }
-#pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const int r = wn * TN + i * 32 + l32;
-      offb[s][i] = AB + r * (KB * 2) + ((2 * s + hh) ^ ((r >> 1) & 7)) * 16;
-    }
+    oa[s] = (uint32_t)((wm * TM + l32) * (KB * 2) + ((2 * s + hh) ^ swz) * 16);
+    ob[s] = (uint32_t)(AB + (wn * TN + l32) * (KB * 2) + ((2 * s + hh) ^ swz) * 16);
   }
   // fragment read x of a k-step, in the order the step's MFMAs first use them (w0 a0 w1 .. a1 ..;
   // the MFMAs run over the weight fragments in the inner loop)
-  auto rd = [&](const char* st, int s, int x, bf16x8* fa, bf16x8* fw) {
+  auto rd_at = [&](const char* st, uint32_t a_off, uint32_t b_off, int x, bf16x8* fa, bf16x8* fw) {
     if (x == 0)
-      fw[0] = *reinterpret_cast<const bf16x8*>(st + offb[s][0]);
+      fw[0] = *reinterpret_cast<const bf16x8*>(st + b_off);
     else if (x == 1)
-      fa[0] = *reinterpret_cast<const bf16x8*>(st + offa[s][0]);
+      fa[0] = *reinterpret_cast<const bf16x8*>(st + a_off);
     else if (x < FN + 1)
-      fw[x - 1] = *reinterpret_cast<const bf16x8*>(st + offb[s][x - 1]);
+      fw[x - 1] = *reinterpret_cast<const bf16x8*>(st + b_off + (x - 1) * FRAG);
     else
-      fa[x - FN] = *reinterpret_cast<const bf16x8*>(st + offa[s][x - FN]);
+      fa[x - FN] = *reinterpret_cast<const bf16x8*>(st + a_off + (x - FN) * FRAG);
   };
-  // The LDS addresses of k-step 0's reads of the next slab, worked out during the current slab's
-  // last k-step so that those reads issue straight after the slab barrier.
+  auto rd = [&](const char* st, int s, int x, bf16x8* fa, bf16x8* fw) { rd_at(st, oa[s], ob[s], x, fa, fw); };
+  // The LDS addresses of k-step 0's fragment 0 reads of the next slab (A and weight), worked out
+  // during the current slab's last k-step so that the reads issue straight after the slab barrier.
   int stage = 0;  // g % NST
-  uint32_t nx[NR];
+  uint32_t nxa = 0, nxb = 0;
   auto set_next = [&](int st) {
-#pragma unroll
-    for (int x = 0; x < NR; ++x)
-      nx[x] = lds0 + (uint32_t)(st * SB) +
-              (uint32_t)(x == 0 ? offb[0][0] : x == 1 ? offa[0][0] : x < FN + 1 ? offb[0][x - 1] : offa[0][x - FN]);
+    nxa = lds0 + (uint32_t)(st * SB) + oa[0];
+    nxb = lds0 + (uint32_t)(st * SB) + ob[0];
   };
   auto rd0 = [&](int x, bf16x8* fa, bf16x8* fw) {
-    const bf16x8 v = *reinterpret_cast<MOSS_LDS const bf16x8*>((size_t)nx[x]);
+    const uint32_t addr = x == 0 ? nxb : x == 1 ? nxa : x < FN + 1 ? nxb + (x - 1) * FRAG : nxa + (x - FN) * FRAG;
+    const bf16x8 v = *reinterpret_cast<MOSS_LDS const bf16x8*>((size_t)addr);
     if (x == 0)
       fw[0] = v;
     else if (x == 1)
