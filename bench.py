@@ -32,7 +32,9 @@ flushed before every forward (``step_times_cold_cache``: a 512 MB fill, which
 also leaves dirty lines for the forward's reads to evict;
 ``step_times_cold_read``: a 512 MB read, which does not); the modulation GEMV
 and the norm each alone beside a torch kernel moving the same bytes
-(``hbm_reference``); the 24-block guidance-pair stack (two items of
+(``hbm_reference``); the up projection's product through this library and
+through torch's linear, i.e. hipBLASLt (``gemm_reference``; alone with
+``--gemm-reference``, for counter runs over both); the 24-block guidance-pair stack (two items of
 4096 image + 34 text rows) in ms per call; the larger pictures (block and
 attention time against the square of the row count); and the block replayed
 from a captured HIP graph.
@@ -89,6 +91,9 @@ def parse():
                    help="write the HBM traffic summary from two rocprofv3 --pmc CSV runs, then exit")
     p.add_argument("--trace-summary", metavar="DB",
                    help="print the per-kernel table of a rocprofv3 --kernel-trace database (results.db), then exit")
+    p.add_argument("--gemm-reference", action="store_true",
+                   help="time the up projection's product through this library and through torch's linear "
+                        "(hipBLASLt) only, print one JSON line, then exit (for counter runs over both)")
     p.add_argument("--counter-summary", nargs="+", metavar="DIR",
                    help="write the MFMA / LDS / wait counter summary from rocprofv3 --pmc CSV runs, then exit")
     return p.parse_args()
@@ -467,6 +472,41 @@ def hbm_reference(torch, moss, geom, reps=15):
     return res
 
 
+def gemm_reference(torch, moss, geom, reps=20):
+    """The up projection's product (rows x 2F x D) through this library's SiLU-gated GEMM and through
+    torch.nn.functional.linear (hipBLASLt on ROCm) on the same bf16 operands, each timed between events
+    on the stream, median of `reps` (the library's kernel also applies the SiLU gate and stores the
+    half-width z; torch's linear stores all 2F columns of the plain product)."""
+    d, f, m = geom.d_model, geom.mlp_inner, geom.batch * geom.rows
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2)
+    a = torch.randn(m, d, generator=g, device="cuda").to(torch.bfloat16)
+    w = (torch.randn(2 * f, d, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    z = torch.empty(m, f, dtype=torch.bfloat16, device="cuda")
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(1000.0 * e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    t_ours = timed(lambda: moss.moss_k_gemm_silu(m, f, d, a, d, w, d, z, f))
+    t_ref = timed(lambda: torch.nn.functional.linear(a, w))
+    gflop = 2.0 * m * 2 * f * d / 1e9
+    del a, w, z
+    torch.cuda.empty_cache()
+    return {"shape": [m, 2 * f, d], "us": round(t_ours, 1), "tflops": round(gflop / t_ours * 1e3, 1),
+            "torch_linear_us": round(t_ref, 1), "torch_linear_tflops": round(gflop / t_ref * 1e3, 1),
+            "torch_linear_kernel": "torch.nn.functional.linear (hipBLASLt), plain product, no epilogue"}
+
+
 def timed_steps(torch, step, out, stream, steps):
     """Run `steps` steps, each between its own pair of events on the launch stream.  After each
     step (outside its events) its output is copied into a device ring; after the loop every copy
@@ -727,6 +767,9 @@ def main():
         raise SystemExit(f"device 0: {moss.moss_status_string(rc)}")
 
     geom = synth.CONFIGS[args.workload]
+    if args.gemm_reference:
+        print(json.dumps({"gemm_reference": gemm_reference(torch, moss, geom)}))
+        return
     acts = synth.make_activations(geom, args.seed)
     wbits = synth.make_block_weights(geom, args.seed, 0)
 
@@ -776,6 +819,7 @@ def main():
         extras["step_times_cold_cache"] = per_step(torch, moss, step, geom, cold="write")
         extras["step_times_cold_read"] = per_step(torch, moss, step, geom, cold="read")
         extras["hbm_reference"] = hbm_reference(torch, moss, geom)
+        extras["gemm_reference"] = gemm_reference(torch, moss, geom)
         extras["stack_c4"] = stack_timing(torch, moss, synth.CONFIGS["c4"], args.seed)
         extras["larger_pictures"] = larger_pictures(torch, moss, w, args.seed)
 
