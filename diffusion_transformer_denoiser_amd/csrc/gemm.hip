@@ -10,16 +10,22 @@
 //  * K advances 64 at a time through two LDS stages (128 KiB for the 256 x 256
 //    tiles; launches of one tile per workgroup whose tiles leave room use
 //    three or four).  Each slab is fetched straight into LDS with
-//    buffer_load_dwordx4 ... lds (issued from asm, see dma16_buf), the next
-//    slab's loads spread evenly over the MFMAs of the current slab's first
-//    two k16 steps, so they have the last two steps to land before the slab's
-//    one barrier.  A slab row is 128 bytes: every load covers whole cache
-//    lines (32-k slabs read half lines, twice as many L2 requests; 4096 x
-//    24576 x 3072 went from 519 to 483 us standalone with this scheme).
+//    buffer_load_dwordx4 ... lds (issued from asm, see dma16_buf_so), the
+//    next slab's loads spread evenly over the MFMAs of the current slab's
+//    first two k16 steps, so they have the last two steps to land before the
+//    slab's one barrier.  A slab row is 128 bytes: every load covers whole
+//    cache lines (32-k slabs read half lines, twice as many L2 requests;
+//    4096 x 24576 x 3072 went from 519 to 483 us standalone with this scheme).
 //  * The MFMA operands of the next k16 step are read from LDS into registers
 //    during the current one, one read after each of its first MFMAs; nothing
 //    is reordered across those points (sched_barrier), so the reads, loads
 //    and MFMAs issue interleaved in the order written.
+//  * Few instructions between two MFMAs (a wavefront issues at most one
+//    every few cycles, an MFMA runs 32): a load is four instructions (no
+//    branch; the k offset in the scalar offset), a lane's fragment reads
+//    share one base per k16 step, the next slab's first read addresses are
+//    ready before the barrier, and a tile's first k-step adds to zero rather
+//    than to cleared registers.
 //  * The 16-byte chunk c of row r is stored at c ^ ((r >> 1) & 7), so the 16
 //    rows a 16-lane group reads for one operand fragment land in 16 distinct
 //    16-byte slots of the LDS banks.
