@@ -371,7 +371,8 @@ int moss_k_gated_add(int32_t batch, int32_t rows, int32_t d_model, float* h, con
 #define MOSS_NUM_STEPS 13
 
 /* Arm the probe: from the next launch of step `step` by moss_block_forward /
- * moss_stack_forward (any stream, this process) on, launches 0, every,
+ * moss_stack_forward (and, for MOSS_STEP_ADALN, the GEMV launch of
+ * moss_k_adaln_gemv; any stream, this process) on, launches 0, every,
  * 2 every, ... of that step, up to `max_launches` of them, are bracketed by
  * HIP events recorded on the launch stream (timing-only events: no
  * system-scope fence; each record still takes a few microseconds of stream
