@@ -551,7 +551,7 @@ def timed_steps(torch, step, out, stream, steps):
     return ms, loop0.elapsed_time(loop1) / steps, wall, identical, digest
 
 
-def larger_pictures(torch, moss, w, seed, reps=20):
+def larger_pictures(torch, moss, w, seed, reps=20, warm=20, settle=40):
     """Block and attention time at 4096 image rows and at the larger pictures of the CUDA port
     page's served-picture table (1280x1024, 1408x1024, 1536x1024: 5120, 5632 and 6144 image
     rows), with the attention time per square row relative to the 4096-row block."""
@@ -575,9 +575,14 @@ def larger_pictures(torch, moss, w, seed, reps=20):
         def step():
             moss.moss_block_forward(dims, x, txt, acts["txt_len"], cond, w, rope, out, ws)
 
-        for _ in range(3):
+        for _ in range(warm):
             step()
         ms, _, _, same, _ = timed_steps(torch, step, out, torch.cuda.current_stream(), reps)
+        # the timed loop's copies into its output ring leave the caches full of dirty lines, and the
+        # forwards after it pay to write them back (the 4096-row attention probe read 277 us on the
+        # first, 233-238 after 10 plain forwards, 226-227 after 40, as the per-step probe does)
+        for _ in range(settle):
+            step()
         moss.moss_probe_arm("ATTN", 5)
         for _ in range(5):
             step()
