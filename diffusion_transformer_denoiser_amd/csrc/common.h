@@ -107,16 +107,11 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
   return r;
 }
 
-// As dma16, through a buffer load: 16 bytes per lane from byte offset voff of the buffer rsrc
-// into LDS at lds + 16 lane (buffer_load_dwordx4 ... lds; bounds-checked by the resource).
-__device__ __forceinline__ void dma16_buf(uint32_t voff, u32x4 rsrc, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(rsrc)
-               : "memory");
-}
-
-// As dma16_buf, the byte offset split into a per-lane part (voff) and a wave-uniform part (soff,
-// the buffer instruction's scalar offset: no per-lane add).  The resource's bounds check covers voff
-// only, so the caller keeps voff + soff in bounds itself.
+// As dma16, through a buffer load: 16 bytes per lane into LDS at lds + 16 lane
+// (buffer_load_dwordx4 ... lds) from byte offset voff + soff of the buffer rsrc, the offset split
+// into a per-lane part (voff) and a wave-uniform part (soff, the instruction's scalar offset: no
+// per-lane add).  The resource's bounds check covers voff only, so the caller keeps voff + soff in
+// bounds itself.
 __device__ __forceinline__ void dma16_buf_so(uint32_t voff, u32x4 rsrc, uint32_t soff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(rsrc),
                "s"(soff)
