@@ -9,7 +9,12 @@
 //
 //  * K advances 64 at a time through two LDS stages (128 KiB for the 256 x 256
 //    tiles; launches of one tile per workgroup whose tiles leave room use
-//    three or four).  Each slab is fetched straight into LDS with
+//    three or four).  In the 256 x 256 and 224 x 256 launches (but QKV's,
+//    whose epilogue borrows a whole stage) the weight tiles have a ring of
+//    their own, one stage deeper, in the LDS the two A stages leave (160 and
+//    152 KiB in all), and are loaded two slabs ahead: with one slab of
+//    lead the waves waited on them (the down projection 296 -> 280 us, out
+//    89 -> 83 us, same-box A/B).  Each slab is fetched straight into LDS with
 //    buffer_load_dwordx4 ... lds (issued from asm, see dma16_buf_so), the
 //    next slab's loads spread evenly over the MFMAs of the current slab's
 //    first two k16 steps, so they have the last two steps to land before the
@@ -401,7 +406,7 @@ __device__ __forceinline__ void epilogue_qkv(const f32x16 (&acc)[BN / WN / 32][B
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int NST = 2, int GRP = kGroupN>
+template <int BM, int BN, int WM, int WN, int EPI, int NST = 2, int GRP = kGroupN, int NSW = NST>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __restrict__ a, int lda,
                                                              const uint16_t* __restrict__ w, int ldw,
                                                              uint16_t* __restrict__ c, int ldc, int m_begin,
@@ -418,8 +423,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
   constexpr int PER = LA + LB;
   static_assert(CA * 1024 == AB && LB * NW * 1024 == BB, "slab / wavefront mismatch");
   static_assert(EPI != kSiluGate || FN % 2 == 0, "the SiLU epilogue pairs gate and up fragments per wavefront");
-  static_assert(NST >= 2 && (NST - 2) * PER <= 63, "stages, and the loads a slab wait leaves in flight");
-  __shared__ __attribute__((aligned(1024))) char smem[NST * SB];
+  // NSW == NST: stage s holds slab s's A tile then its weight tile.  NSW == NST + 1: the weight
+  // tiles get a ring of their own, one stage deeper, after the NST A stages, and are loaded one
+  // slab further ahead than the A tiles.
+  static_assert(NSW == NST || NSW == NST + 1, "weight stages: as many as the A stages, or one more");
+  constexpr bool SPLIT = NSW != NST;
+  constexpr int INFL = (NST - 2) * PER + (SPLIT ? LB : 0);  // loads a slab wait leaves in flight
+  static_assert(NST >= 2 && INFL <= 63, "stages, and the loads a slab wait leaves in flight");
+  __shared__ __attribute__((aligned(1024))) char smem[NST * AB + NSW * BB];
+  constexpr auto a_base = [](int st) { return (uint32_t)(SPLIT ? st * AB : st * SB); };
+  constexpr auto w_base = [](int st) { return (uint32_t)(SPLIT ? NST * AB + st * BB : st * SB + AB); };
 
   // This launch covers rows [m_begin, m).  Workgroup b computes tiles b, b + G, b + 2G, ... of the
   // launch (G workgroups); the loads run on from one of its tiles into the next, so a tile's first
@@ -442,17 +455,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
 #pragma unroll
   for (int i = 0; i < LA; ++i) ca[i] = 1024u * min(wv + NW * i, CA - 1);
   uint32_t va[LA], vb[LB];  // byte offsets of this lane's 16 bytes of slab 0 of the current tile
-  auto aim = [&](int r) {    // point the loads at this workgroup's tile r
+  auto aim = [&](int r, bool do_a, bool do_w) {  // point the A (weight) loads at this workgroup's tile r
     int tm, tn;
     tile_of<GRP>(blockIdx.x + r * G, mt, ntn, tm, tn);
     const int m0 = m_begin + tm * BM, n0 = tn * BN;
 #pragma unroll
-    for (int i = 0; i < LA; ++i) {
+    for (int i = 0; i < LA && do_a; ++i) {
       const int rr = min(wv + NW * i, CA - 1) * 8 + (lane >> 3);
       va[i] = (uint32_t)(((size_t)min(m0 + rr, m - 1) * lda + ((lane & 7) ^ ((rr >> 1) & 7)) * 8) * 2);
     }
 #pragma unroll
-    for (int i = 0; i < LB; ++i) {
+    for (int i = 0; i < LB && do_w; ++i) {
       const int rr = (wave + NW * i) * 8 + (lane >> 3);
       int wrow = n0 + rr;
       if (EPI == kSiluGate) {
@@ -466,18 +479,41 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
     }
   };
   const uint32_t lds0 = (uint32_t)(uintptr_t)(MOSS_LDS char*)smem;
-  int lt = 0, lk = 0, lst = 0;  // the next slab to load: tile, slab within it, stage
+  int lt = 0, lk = 0, lst = 0;     // the next slab to load: tile, slab within it, stage
+  int ltw = 0, lkw = 0, lstw = 0;  // with a weight ring of its own: the next weight slab
   auto issue_one = [&](int q) {  // load instruction q of that slab; the last one moves on
-    const uint32_t base = lds0 + (uint32_t)(lst * SB), koff = (uint32_t)(lk * (KB * 2));
-    if (q < LA)
-      dma16_buf_so(va[q], ra, koff, base + ca[q]);
-    else
-      dma16_buf_so(vb[q - LA], rw, koff, base + AB + 1024u * (wv + NW * (q - LA)));
-    if (q == PER - 1) {
-      lst = lst + 1 == NST ? 0 : lst + 1;
-      if (++lk == nk) {
-        lk = 0;
-        if (++lt < mine) aim(lt);
+    if constexpr (!SPLIT) {
+      const uint32_t base = lds0 + (uint32_t)(lst * SB), koff = (uint32_t)(lk * (KB * 2));
+      if (q < LA)
+        dma16_buf_so(va[q], ra, koff, base + ca[q]);
+      else
+        dma16_buf_so(vb[q - LA], rw, koff, base + AB + 1024u * (wv + NW * (q - LA)));
+      if (q == PER - 1) {
+        lst = lst + 1 == NST ? 0 : lst + 1;
+        if (++lk == nk) {
+          lk = 0;
+          if (++lt < mine) aim(lt, true, true);
+        }
+      }
+    } else {
+      if (q < LA) {
+        dma16_buf_so(va[q], ra, (uint32_t)(lk * (KB * 2)), lds0 + a_base(lst) + ca[q]);
+        if (q == LA - 1) {
+          lst = lst + 1 == NST ? 0 : lst + 1;
+          if (++lk == nk) {
+            lk = 0;
+            if (++lt < mine) aim(lt, true, false);
+          }
+        }
+      } else {
+        dma16_buf_so(vb[q - LA], rw, (uint32_t)(lkw * (KB * 2)), lds0 + w_base(lstw) + 1024u * (wv + NW * (q - LA)));
+        if (q == PER - 1) {
+          lstw = lstw + 1 == NSW ? 0 : lstw + 1;
+          if (++lkw == nk) {
+            lkw = 0;
+            if (++ltw < mine) aim(ltw, false, true);
+          }
+        }
       }
     }
   };
@@ -492,28 +528,32 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     oa[s] = (uint32_t)((wm * TM + l32) * (KB * 2) + ((2 * s + hh) ^ swz) * 16);
-    ob[s] = (uint32_t)(AB + (wn * TN + l32) * (KB * 2) + ((2 * s + hh) ^ swz) * 16);
+    ob[s] = (uint32_t)((wn * TN + l32) * (KB * 2) + ((2 * s + hh) ^ swz) * 16);
   }
   // fragment read x of a k-step, in the order the step's MFMAs first use them (w0 a0 w1 .. a1 ..;
   // the MFMAs run over the weight fragments in the inner loop)
-  auto rd_at = [&](const char* st, uint32_t a_off, uint32_t b_off, int x, bf16x8* fa, bf16x8* fw) {
+  auto rd_at = [&](const char* sa, const char* sw, uint32_t a_off, uint32_t b_off, int x, bf16x8* fa, bf16x8* fw) {
     if (x == 0)
-      fw[0] = *reinterpret_cast<const bf16x8*>(st + b_off);
+      fw[0] = *reinterpret_cast<const bf16x8*>(sw + b_off);
     else if (x == 1)
-      fa[0] = *reinterpret_cast<const bf16x8*>(st + a_off);
+      fa[0] = *reinterpret_cast<const bf16x8*>(sa + a_off);
     else if (x < FN + 1)
-      fw[x - 1] = *reinterpret_cast<const bf16x8*>(st + b_off + (x - 1) * FRAG);
+      fw[x - 1] = *reinterpret_cast<const bf16x8*>(sw + b_off + (x - 1) * FRAG);
     else
-      fa[x - FN] = *reinterpret_cast<const bf16x8*>(st + a_off + (x - FN) * FRAG);
+      fa[x - FN] = *reinterpret_cast<const bf16x8*>(sa + a_off + (x - FN) * FRAG);
   };
-  auto rd = [&](const char* st, int s, int x, bf16x8* fa, bf16x8* fw) { rd_at(st, oa[s], ob[s], x, fa, fw); };
+  auto rd = [&](const char* sa, const char* sw, int s, int x, bf16x8* fa, bf16x8* fw) {
+    rd_at(sa, sw, oa[s], ob[s], x, fa, fw);
+  };
   // The LDS addresses of k-step 0's fragment 0 reads of the next slab (A and weight), worked out
   // during the current slab's last k-step so that the reads issue straight after the slab barrier.
   int stage = 0;  // g % NST
+  int stw = 0;    // g % NSW (the weight stage, with a weight ring of its own)
+  auto wstage = [&]() { return SPLIT ? stw : stage; };
   uint32_t nxa = 0, nxb = 0;
-  auto set_next = [&](int st) {
-    nxa = lds0 + (uint32_t)(st * SB) + oa[0];
-    nxb = lds0 + (uint32_t)(st * SB) + ob[0];
+  auto set_next = [&](int sa, int sw) {
+    nxa = lds0 + a_base(sa) + oa[0];
+    nxb = lds0 + w_base(sw) + ob[0];
   };
   auto rd0 = [&](int x, bf16x8* fa, bf16x8* fw) {
     const uint32_t addr = x == 0 ? nxb : x == 1 ? nxa : x < FN + 1 ? nxb + (x - 1) * FRAG : nxa + (x - FN) * FRAG;
@@ -527,17 +567,22 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
     else
       fa[x - FN] = v;
   };
-  set_next(0);
+  set_next(0, 0);
 
-  // the first NST - 1 slabs; then wait for slab 0 alone
-  aim(0);
+  // the first NST - 1 slabs (and, with a weight ring of its own, the weight tile of one more);
+  // then wait for slab 0 alone
+  aim(0, true, true);
 #pragma unroll
   for (int sl = 0; sl < NST - 1; ++sl)
     if (sl < total)
 #pragma unroll
       for (int q = 0; q < PER; ++q) issue_one(q);
-  if (NST > 2 && total >= NST - 1)
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NST - 2) * PER) : "memory");
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int q = LA; q < PER; ++q) issue_one(q);
+  }
+  if (INFL > 0 && total >= NSW - 1)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(INFL) : "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
@@ -560,7 +605,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
       // slab g + NST - 1 is loaded during steps 0-1.  Past a workgroup's last slab the loads go on
       // without a test (no branch among the MFMAs): they read rows of its last tile again, in
       // bounds, into the stage of a slab already consumed, and the last slab waits for them.
-      const char* cur = smem + stage * SB;
+      const char* cur = smem + a_base(stage);
+      const char* curw = smem + w_base(wstage());
       bf16x8 fa[2][FM], fw[2][FN];
 #pragma unroll
       for (int x = 0; x < NR; ++x) {
@@ -582,9 +628,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
           if (s < 3) {
 #pragma unroll
             for (int x = t; x < (t + 1 == NMF ? NR : t + 1); ++x)
-              if (x < NR) rd(cur, s + 1, x, fa[(s + 1) & 1], fw[(s + 1) & 1]);
+              if (x < NR) rd(cur, curw, s + 1, x, fa[(s + 1) & 1], fw[(s + 1) & 1]);
           }
-          if (s == 3 && t == 0) set_next(stage + 1 == NST ? 0 : stage + 1);
+          if (s == 3 && t == 0)
+            set_next(stage + 1 == NST ? 0 : stage + 1, SPLIT ? (stw + 1 == NSW ? 0 : stw + 1) : (stage + 1 == NST ? 0 : stage + 1));
           if (s < 2) {
             const int u = s * NMF + t;
 #pragma unroll
@@ -596,11 +643,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
       // slab g + 1 resident and every read of slab g done before the next slab's loads overwrite it.
       // Loads complete in order, so leaving the newest (NST - 2) * PER (the slabs after g + 1) in
       // flight is exact; epilogue stores issued in between only make the wait longer.
-      if (NST > 2 && g + NST - 1 < total)
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NST - 2) * PER) : "memory");
+      if (INFL > 0 && g + NSW - 1 < total)
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(INFL) : "memory");
       else
         asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
       stage = stage + 1 == NST ? 0 : stage + 1;
+      if constexpr (SPLIT) stw = stw + 1 == NSW ? 0 : stw + 1;
       ++g;
     };
     slab(std::true_type{});  // nk >= 1: the launcher refuses k < 64
@@ -608,6 +656,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
 
     if constexpr (EPI == kQkvPack) {
       // the stage of the tile's last slab stays free until the next tile's slab NST - 1 is loaded
+      static_assert(!SPLIT, "the q/k epilogue takes a whole stage as its spare");
       char* spare = smem + ((g + NST - 1) % NST) * SB;
       epilogue_qkv<BM, BN, WM, WN>(acc, spare, m0, n0, wave, wm, wn, l32, hh, m, ep);
     } else if constexpr (EPI == kGatedAdd && WM == 1 && WN == 8 && BN == 256 && NST == 2) {
@@ -683,14 +732,14 @@ hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_
       // 224 x 64 (1 per SIMD) kept less.
       const int t256 = ((m + 255) / 256) * nt, t224 = ((m + 223) / 224) * nt;
       if (!split && (t224 + cus - 1) / cus == (t256 + cus - 1) / cus) {
-        hipLaunchKernelGGL((gemm_nt_kernel<224, 256, 1, 8, EPI, 2, kGroupNGated>), dim3(t224), dim3(512), 0, st, a, lda, w, ldw, c,
+        hipLaunchKernelGGL((gemm_nt_kernel<224, 256, 1, 8, EPI, 2, kGroupNGated, 3>), dim3(t224), dim3(512), 0, st, a, lda, w, ldw, c,
                            ldc, 0, m, n, k, ep);
         return hipGetLastError();
       }
     }
     // one workgroup per CU, each taking every cus-th tile
     constexpr int grp = EPI == kSiluGate ? kGroupNUp : kGroupN;
-    hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI, 2, grp>), dim3(std::min(((m_main + 255) / 256) * nt, cus)),
+    hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI, 2, grp, EPI == kQkvPack ? 2 : 3>), dim3(std::min(((m_main + 255) / 256) * nt, cus)),
                        dim3(512), 0, st, a, lda, w, ldw, c, ldc, 0, m_main, n, k, ep);
     if (split) {
       // The tail is bound by reading all of w once: more workgroups, and more slabs in flight per
