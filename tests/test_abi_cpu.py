@@ -166,6 +166,7 @@ def test_single_step_entry_points_validate():
     L = moss.lib()
     assert L.moss_k_gemm_nt(100, 200, 256, fake(1), 256, fake(2), 256, fake(3), 200, None) == moss.MOSS_EINVAL
     assert L.moss_k_gemm_nt(100, 256, 192, fake(1), 192, fake(2), 192, fake(3), 256, None) == moss.MOSS_EINVAL
+    assert L.moss_k_gemm_nt(100, 256, 64, fake(1), 64, fake(2), 64, fake(3), 256, None) == moss.MOSS_EINVAL
     assert L.moss_k_gemm_nt(100, 256, 256, fake(1), 100, fake(2), 256, fake(3), 256, None) == moss.MOSS_EINVAL
     assert L.moss_k_gemm_nt(100, 256, 256, fake(1), 256, fake(2), 256, fake(1, 512), 256, None) == moss.MOSS_EALIAS
     assert L.moss_k_silu_mul(10, 100, fake(1), fake(2), None) == moss.MOSS_EINVAL

@@ -110,6 +110,11 @@ def test_mod_rmsnorm(batch, rows, d):
     # after the whole rounds (the 4096+34-row QKV: 30 + 6 column tiles; 1280 rows: 51 + 9)
     (4130, 9216, 3072),
     (1280, 15360, 256),
+    # two 64-k slabs per tile (the smallest K taken), as many as the weight tiles' lead: the
+    # loads past a workgroup's last slab, and (two tiles per workgroup) the weight loads
+    # entering the next tile one slab before the A loads
+    (513, 3072, 128),
+    (2048, 16384, 128),
 ])
 def test_gemm_nt(m, n, k):
     G.say(f"gemm_nt M={m} N={n} K={k}")
@@ -160,7 +165,8 @@ def test_gemm_column_split_strided():
 
 
 @pytest.mark.parametrize("m,f,k", [(72, 1024, 256), (1058, 384, 512), (4130, 12288, 3072), (1124, 8192, 256),
-                                   (4300, 12288, 256)])  # 1632 tiles, one workgroup per CU, a part-full last row tile
+                                   (4300, 12288, 256),  # 1632 tiles, one workgroup per CU, a part-full last row tile
+                                   (1124, 8192, 128)])  # two slabs per tile
 def test_gemm_silu(m, f, k):
     """The up projection with the SiLU gate in its epilogue (a9 + a10 as the block runs them)."""
     G.say(f"gemm_silu M={m} F={f} K={k}")
@@ -177,7 +183,9 @@ def test_gemm_silu(m, f, k):
 
 @pytest.mark.parametrize("batch,rows,n,k", [(1, 72, 256, 256), (2, 530, 384, 512), (2, 4130, 3072, 12288),
                                             (2, 529, 16384, 256),
-                                            (1, 2048, 16384, 256)])  # 256x256 tiles, two per workgroup
+                                            (1, 2048, 16384, 256),  # 256x256 tiles, two per workgroup
+                                            (1, 300, 512, 128),  # 224-row tiles, two slabs each
+                                            (1, 2048, 16384, 128)])  # 256x256 tiles, two per workgroup, two slabs each
 @pytest.mark.parametrize("to_bf16", [False, True])
 def test_gemm_gated_add(batch, rows, n, k, to_bf16):
     """The out / down projection with the gated residual add in its epilogue (a6 + a7, a11 + a12)."""
