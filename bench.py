@@ -66,7 +66,7 @@ CALIB_BYTES = 256 << 20  # the plain device copy the counters are scaled by
 PROBE_EVERY = 5  # the timed steps whose up projection the probe brackets: 0, 5, 10, ...
 # the up projection with the SiLU gate epilogue: whole 256-row tiles (two LDS stages), then the 34 leftover rows
 # as 64 x 64 tiles (four stages)
-UP_KERNELS = ("gemm_nt_kernel<256, 256, 2, 4, 1, 2, 16, 3>", "gemm_nt_kernel<64, 64, 2, 1, 1, 4, 6, 4>")
+UP_KERNELS = ("gemm_nt_kernel<256, 256, 2, 4, 1, 2, 6, 3>", "gemm_nt_kernel<64, 64, 2, 1, 1, 4, 6, 4>")
 GEMM_SOURCES = ("diffusion_transformer_denoiser_amd/csrc/gemm.hip", "diffusion_transformer_denoiser_amd/csrc/common.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_up_c2_traffic.md")
 METRIC = "denoiser block-forwards/s and TFLOP/s at 4096+34 tokens; MFMA % of peak"

@@ -34,10 +34,9 @@
 //  * The 16-byte chunk c of row r is stored at c ^ ((r >> 1) & 7), so the 16
 //    rows a 16-lane group reads for one operand fragment land in 16 distinct
 //    16-byte slots of the LDS banks.
-//  * Tiles are numbered in groups of six column tiles (sixteen for the up
-//    projection), row-major within a group, and workgroup ids (dealt
-//    round-robin over the 8 XCDs) are remapped so each XCD runs a contiguous
-//    stretch of that order: with groups of six, the ~32 tiles an XCD holds at
+//  * Tiles are numbered in groups of six column tiles, row-major within a
+//    group, and workgroup ids (dealt round-robin over the 8 XCDs) are
+//    remapped so each XCD runs a contiguous stretch of that order: with groups of six, the ~32 tiles an XCD holds at
 //    once span about 5 row and 6 column panels, which its L2 shares (fetch
 //    from beyond L2 down ~40% from an M-fastest order).
 //  * The weight tile is the MFMA's first operand and the activation tile the
@@ -94,12 +93,12 @@ struct EpiArgs {
   int col0;           // kQkvPack: absolute column of this launch's column 0
 };
 
-// Column tiles per group of the tile order.  The up projection's whole tiles (96 column tiles)
-// take groups of 16: 4 us faster than 6 over two interleaved same-box runs (12: the same, 24 and
-// 48 slower); QKV's and the out and down projections' sweeps (3, 4, 10, 12, 15) stayed within
-// the runs' 1% spread, so they keep 6.
+// Column tiles per group of the tile order.  For the up projection's whole tiles (96 column
+// tiles) groups of 3 to 6 run level and 16 lose 0.9% per block (two interleaved same-box runs
+// each; 16 had won 4 us over 6 before the weight tiles' ring of their own, which made the loads
+// the waves wait on fewer); QKV's and the out and down projections' sweeps (3, 4, 10, 12, 15)
+// stayed within the runs' 1% spread.
 constexpr int kGroupN = 6;
-constexpr int kGroupNUp = 16;
 constexpr int kGroupNQkv = 6;
 constexpr int kGroupNGated = 6;
 
@@ -738,8 +737,7 @@ hipError_t launch(int m, int n, int k, const uint16_t* a, int lda, const uint16_
       }
     }
     // one workgroup per CU, each taking every cus-th tile
-    constexpr int grp = EPI == kSiluGate ? kGroupNUp : kGroupN;
-    hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI, 2, grp, EPI == kQkvPack ? 2 : 3>), dim3(std::min(((m_main + 255) / 256) * nt, cus)),
+    hipLaunchKernelGGL((gemm_nt_kernel<256, 256, 2, 4, EPI, 2, kGroupN, EPI == kQkvPack ? 2 : 3>), dim3(std::min(((m_main + 255) / 256) * nt, cus)),
                        dim3(512), 0, st, a, lda, w, ldw, c, ldc, 0, m_main, n, k, ep);
     if (split) {
       // The tail is bound by reading all of w once: more workgroups, and more slabs in flight per
