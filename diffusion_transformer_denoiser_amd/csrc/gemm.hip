@@ -601,9 +601,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt and expcnt unconstrained
     auto slab = [&](auto first_slab) {
       constexpr bool FIRST = decltype(first_slab)::value;
-      // slab g + NST - 1 is loaded during steps 0-1.  Past a workgroup's last slab the loads go on
-      // without a test (no branch among the MFMAs): they read rows of its last tile again, in
-      // bounds, into the stage of a slab already consumed, and the last slab waits for them.
+      // the A tile of slab g + NST - 1 and the weight tile of slab g + NSW - 1 are loaded during
+      // steps 0-1, the A loads first.  Past a workgroup's last slab the loads go on without a test
+      // (no branch among the MFMAs): they read rows of its last tile again, in bounds, into the
+      // stage of a slab already consumed, and the last slabs wait for them.
       const char* cur = smem + a_base(stage);
       const char* curw = smem + w_base(wstage());
       bf16x8 fa[2][FM], fw[2][FN];
@@ -640,8 +641,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_nt_kernel(const uint16_t* __
         }
       }
       // slab g + 1 resident and every read of slab g done before the next slab's loads overwrite it.
-      // Loads complete in order, so leaving the newest (NST - 2) * PER (the slabs after g + 1) in
-      // flight is exact; epilogue stores issued in between only make the wait longer.
+      // Loads complete in order, so leaving the newest INFL in flight is exact: the (NST - 2) * PER
+      // of the slabs after g + 1 and, with a weight ring of its own, the weight loads issued after
+      // slab g + 1's A loads; epilogue stores issued in between only make the wait longer.
       if (INFL > 0 && g + NSW - 1 < total)
         asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(INFL) : "memory");
       else
