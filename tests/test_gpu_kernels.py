@@ -185,6 +185,7 @@ def test_gemm_silu(m, f, k):
                                             (2, 529, 16384, 256),
                                             (1, 2048, 16384, 256),  # 256x256 tiles, two per workgroup
                                             (1, 300, 512, 128),  # 224-row tiles, two slabs each
+                                            (2, 4130, 3072, 128),  # 224-row tiles, two per workgroup, two slabs each
                                             (1, 2048, 16384, 128)])  # 256x256 tiles, two per workgroup, two slabs each
 @pytest.mark.parametrize("to_bf16", [False, True])
 def test_gemm_gated_add(batch, rows, n, k, to_bf16):
