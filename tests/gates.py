@@ -22,6 +22,7 @@ QKV_PACK_SHAPES = [
     (1, 8, 8, 8, 2),      # one 128-row tile of rows, two heads
     (2, 34, 8, 12, 3),    # items that straddle row tiles; D = 384: a tile spans q and k columns
     (1, 34, 64, 64, 24),  # the 4096+34-row QKV (column split: the last 6 column tiles run as 128-row tiles)
+    (2, 34, 64, 64, 24),  # the guidance pair's QKV, 2 x 4130 rows, as each block of the stack runs it
 ]
 
 

@@ -340,6 +340,15 @@ def test_attention_24_heads(batch, lens):
     gates.check_attention(got, ref)
 
 
+def test_attention_24_heads_larger_picture():
+    """The 1408 x 1024 picture's attention (5632 image + 34 text rows: 23 query tiles per head, 552
+    workgroups, more than two rounds over the CUs): all 24 heads run; heads 0, 11 and 23 are compared
+    element by element with the oracle."""
+    G.say("attention 24 heads, 5666 rows")
+    got, ref = _attention_case(1, 24, 5666, 34, None, seed=12, ref_heads=(0, 11, 23))
+    gates.check_attention(got, ref)
+
+
 def test_attention_cancellation():
     """Equal scores over values of +-2^22 that cancel, plus a small signal.
 
