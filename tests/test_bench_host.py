@@ -1,8 +1,9 @@
 """bench.py's host logic that turns rocprofv3 output into the committed summaries and into the bench
 line's traffic figure (no GPU): FETCH_SIZE / WRITE_SIZE scaled by what they read for the plain
 256 MiB copy, the up projection's two launches summed per projection, the source-hash guard on the
-stored record, and the counter formulas of the MFMA / wait summary.  Inputs are small synthetic CSVs
-in rocprofv3's column layout."""
+stored record, the counter formulas of the MFMA / wait summary, and the kernel-trace table.  Inputs
+are small synthetic CSVs in rocprofv3's column layout and a database with the two tables the trace
+summary reads."""
 import csv
 import json
 import os
@@ -107,3 +108,32 @@ def test_counter_summary_formulas(tmp_path, monkeypatch):
     assert cells[7] == "10.0%"     # SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES
     assert cells[8] == "20.0%"     # LDS busy
     assert cells[10] == "512"      # 1e8 mops x 512 flops / 100 us, in TFLOP/s
+
+
+def test_trace_summary_groups_dispatches_by_kernel_and_grid(tmp_path, capsys):
+    import sqlite3
+    db = str(tmp_path / "trace.db")
+    c = sqlite3.connect(db)
+    c.execute("create table rocpd_info_kernel_symbol (id integer, display_name text, arch_vgpr_count integer, "
+              "accum_vgpr_count integer, group_segment_size integer)")
+    c.execute("create table rocpd_kernel_dispatch (kernel_id integer, grid_size_x integer, grid_size_y integer, "
+              "workgroup_size_x integer, start integer, end integer)")
+    c.executemany("insert into rocpd_info_kernel_symbol values (?, ?, ?, ?, ?)",
+                  [(1, _full("gemm_nt_kernel<224, 256, 1, 8, 2, 2, 6, 3>"), 128, 0, 155648),
+                   (2, _full("attn_fwd_kernel"), 104, 0, 98304)])
+    # the 224-row launch at two shapes' worth of time (out 80 + 90 us, down 300 us) and the attention twice
+    c.executemany("insert into rocpd_kernel_dispatch values (?, ?, ?, ?, ?, ?)",
+                  [(1, 116736, 1, 512, 0, 80000), (1, 116736, 1, 512, 100000, 190000),
+                   (1, 116736, 1, 512, 200000, 500000),
+                   (2, 8704, 24, 512, 600000, 830000), (2, 8704, 24, 512, 900000, 1130000)])
+    c.commit()
+    c.close()
+    bench.trace_summary(db)
+    rows = [l for l in capsys.readouterr().out.splitlines() if l.startswith("| ") and not l.startswith("| kernel |")]
+    cells = [[x.strip() for x in r.strip("|").split("|")] for r in rows]
+    assert [r[0] for r in cells] == ["gemm_nt_kernel<224, 256, 1, 8, 2, 2, 6, 3>", "attn_fwd_kernel"]  # by total time
+    gemm, attn = cells
+    assert gemm[1:8] == ["116736x1", "512", "128", "0", "155648", "3", "156.7"]  # (80 + 90 + 300) / 3 us
+    assert gemm[8:10] == ["80.0", "300.0"]
+    assert attn[1] == "8704x24" and attn[6:8] == ["2", "230.0"]
+    assert gemm[10] == f"{100 * 470 / 930:.1f}%" and attn[10] == f"{100 * 460 / 930:.1f}%"
